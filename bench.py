@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""MLA decode throughput on one MI355X: tokens/s and achieved latent-cache
+HBM bandwidth.
+
+One step is the whole hot path over one batch: append the new tokens' rows
+to the paged latent cache, fold the queries into latent space, split-KV
+attention over the cache, merge the splits and project out through W_uv.
+Inputs are synthetic and seeded, already resident in HBM when timing starts.
+R copies of {cache, folded weights} (>= 1 GiB together) are used in turn so
+that the 256 MB last-level cache cannot serve a step from the previous one.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv2_b32_ctx4096")
+    ap.add_argument("--kv-chunk", type=int, default=0, help="tokens per split (0 = library's choice)")
+    ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = enough for >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_state(wl, kv_chunk, rotate):
+    import numpy as np
+    import torch
+
+    import mla_compressed_latent_amd as mla
+
+    s = wl.shape
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    dev = "cuda"
+
+    def up(a, dtype=dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dtype)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.int32))).to(dev)
+
+    cfg = mla.config_from_shape(s)
+    w_dkv, w_uk, w_uv = up(wl.w_dkv()), up(wl.w_uk()), up(wl.w_uv())
+    table_np, num_pages = wl.page_table()
+    table = i32(table_np)
+    prefix = wl.prefix_lens()
+    q_lens = wl.q_lens()
+    seq_lens_np = wl.seq_lens()
+    B = wl.batch
+    cache0 = torch.empty((num_pages, s.page_size, s.row_width), dtype=dt, device=dev)
+    layer0 = mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv)
+
+    t0 = time.time()
+    ps = s.page_size
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        if wl.prefix_source == "hidden":
+            group = 8
+            for b0 in range(0, B, group):
+                bs = list(range(b0, min(B, b0 + group)))
+                xs = list(ex.map(wl.prefix_hidden, bs))
+                cu = np.zeros(B + 1, np.int64)
+                for j, b in enumerate(bs):
+                    cu[b + 1] = xs[j].shape[0]
+                x = up(np.concatenate(xs, axis=0))
+                mla.mla_append_latent(layer0, x, i32(np.cumsum(cu)), i32(np.zeros(B)), table, cache0)
+                torch.cuda.synchronize()
+                del x, xs
+        else:
+            futs = {b: ex.submit(wl.prefix_latent, b) for b in range(min(B, 16))}
+            for b in range(B):
+                if b + 16 < B:
+                    futs[b + 16] = ex.submit(wl.prefix_latent, b + 16)
+                rows = up(futs.pop(b).result())
+                P = rows.shape[0]
+                npg = (P + ps - 1) // ps
+                if npg:
+                    pages = torch.from_numpy(table_np[b, :npg].astype(np.int64)).to(dev)
+                    padded = torch.zeros((npg * ps, s.row_width), dtype=dt, device=dev)
+                    padded[:P] = rows
+                    cache0[pages] = padded.view(npg, ps, s.row_width)
+    torch.cuda.synchronize()
+    log(f"prefix cache filled in {time.time() - t0:.1f}s ({wl.prefix_source} prefixes)")
+
+    cache_bytes = cache0.numel() * cache0.element_size()
+    folded_bytes = layer0.folded.numel()
+    R = rotate or max(1, math.ceil((1 << 30) / (cache_bytes + folded_bytes)))
+    layers, caches = [layer0], [cache0]
+    for _ in range(R - 1):
+        layers.append(mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv))
+        caches.append(cache0.clone())
+    del w_dkv, w_uk, w_uv
+    torch.cuda.synchronize()
+
+    Tq = int(q_lens.sum())
+    st = dict(
+        mla=mla, s=s, dt=dt, layers=layers, caches=caches, R=R, table=table, B=B, Tq=Tq,
+        q=up(wl.queries()), x_new=up(wl.new_hidden()), cu_q=i32(wl.cu_q()), prefix=i32(prefix),
+        seq_lens=i32(seq_lens_np), seq_lens_np=seq_lens_np, max_q_len=int(q_lens.max()),
+        max_seq_len=int(seq_lens_np.max()), kv_chunk=kv_chunk,
+        out=torch.empty((Tq, s.H, s.d_v), dtype=dt, device=dev),
+        cache_bytes=cache_bytes, folded_bytes=folded_bytes,
+    )
+    st["chunk"] = mla.mla_decode_kv_chunk(layer0, B, st["max_q_len"], st["max_seq_len"], kv_chunk)
+    st["aws"] = torch.empty(max(1, mla.mla_append_workspace_bytes(layer0, Tq)), dtype=torch.uint8, device=dev)
+    st["dws"] = torch.empty(max(1, mla.mla_decode_workspace_bytes(layer0, B, Tq, st["max_q_len"],
+                                                                  st["max_seq_len"], kv_chunk)),
+                            dtype=torch.uint8, device=dev)
+    return st
+
+
+def run_step(st, i, ev=None):
+    mla = st["mla"]
+    r = i % st["R"]
+    layer, cache = st["layers"][r], st["caches"][r]
+    args = (layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["out"], st["max_q_len"],
+            st["max_seq_len"], st["kv_chunk"], st["dws"])
+    if ev is not None:
+        ev[0].record()
+    mla.mla_append_latent(layer, st["x_new"], st["cu_q"], st["prefix"], st["table"], cache, workspace=st["aws"])
+    if ev is not None:
+        ev[1].record()
+    mla.mla_decode_phases(*args, phases=mla.MLA_PHASE_ABSORB)
+    if ev is not None:
+        ev[2].record()
+    mla.mla_decode_phases(*args, phases=mla.MLA_PHASE_ATTEND)
+    if ev is not None:
+        ev[3].record()
+    mla.mla_decode_phases(*args, phases=mla.MLA_PHASE_OUTPUT)
+    if ev is not None:
+        ev[4].record()
+
+
+def cpu_baseline(wl, budget_s):
+    """The float64 oracle on whole sequences of the same workload, as many as
+    fit in the time budget (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import mla_oracle
+
+    s = wl.shape
+    w_dkv, w_uk, w_uv = wl.w_dkv(), wl.w_uk(), wl.w_uv()
+    scale = mla_oracle.default_scale(s.d_nope, s.d_rope)
+    cores = min(16, os.cpu_count() or 1)
+    done_q = 0
+    elapsed = 0.0
+    seqs = 0
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for b in range(wl.batch):
+            P = int(wl.prefix_lens()[b])
+            if wl.prefix_source == "hidden":
+                pre = mla_oracle.latent_rows(wl.prefix_hidden(b), w_dkv, np.arange(P), s.d_c, s.rope_base)
+            else:
+                pre = wl.prefix_latent(b).astype(np.float64)
+            x_new, q = wl.new_hidden(b), wl.queries(b)
+            t0 = time.perf_counter()
+            new = mla_oracle.latent_rows(x_new, w_dkv, P + np.arange(x_new.shape[0]), s.d_c, s.rope_base)
+            cache = np.concatenate([pre, new], axis=0)
+            mla_oracle.attend_sequence(q, cache, w_uk, w_uv, s.H, s.d_nope, s.d_v, s.rope_base, scale)
+            elapsed += time.perf_counter() - t0
+            done_q += q.shape[0]
+            seqs += 1
+            if elapsed >= budget_s:
+                break
+    return {
+        "value": done_q / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{seqs} of {wl.batch} sequences ({done_q} query tokens, all {s.H} heads), "
+                  f"append + unabsorbed float64 attention, {elapsed:.1f}s",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the decode step runs on a single MI355X and multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mla_synth import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"workload {wl.name}: {wl.description}")
+    st = build_state(wl, args.kv_chunk, args.rotate)
+    log(f"kv_chunk {st['chunk']}, {st['R']} rotated copies of cache ({st['cache_bytes'] / 1e6:.1f} MB) "
+        f"+ folded weights ({st['folded_bytes'] / 1e6:.1f} MB)")
+
+    for i in range(args.warmup):
+        run_step(st, i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        run_step(st, args.warmup + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    phase = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / K for j in range(4)]
+    ms_step = total_ms / K
+    s = st["s"]
+    latent_bytes = int(st["seq_lens_np"].astype("int64").sum()) * s.row_width * (2 if s.dtype == "bf16" else 4)
+    attend_s = phase[2] * 1e-3
+    achieved = latent_bytes / attend_s / 1e9
+    # scores (K = d_c + d_rope) and value sums (K = d_c) per query row and cached token
+    q_lens = wl.q_lens()
+    flops = 2.0 * s.H * (2 * s.d_c + s.d_rope) * float(
+        sum(int(L) * int(lq) for L, lq in zip(st["seq_lens_np"], q_lens)))
+    res = {
+        "metric": METRIC,
+        "value": st["Tq"] * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded Gaussian hidden states / latent rows and weights)",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "query_tokens": st["Tq"],
+            "max_context": st["max_seq_len"], "heads": s.H, "kv_lora_rank": s.d_c,
+            "qk_rope_head_dim": s.d_rope, "kv_chunk": st["chunk"], "rotated_copies": st["R"],
+        },
+        "latent_cache_GBps": achieved,
+        "latent_cache_frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
+        "phase_us": {"append": phase[0] * 1e3, "absorb": phase[1] * 1e3, "attend": phase[2] * 1e3,
+                     "combine_and_output": phase[3] * 1e3},
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "kernel": "split-KV attention (MLA_PHASE_ATTEND)",
+            "algorithmic_bytes_per_launch": latent_bytes,
+            "mfma_tflops": flops / attend_s / 1e12,
+            "mfma_frac_of_bf16_peak": flops / attend_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        },
+    }
+    log(f"{ms_step * 1e3:.1f} us/step, attend {phase[2] * 1e3:.1f} us -> {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak)")
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * mla.h -- C ABI of the MLA (Multi-head Latent Attention) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode layer in its weight-absorbed form.  Each token's cache entry is
+ * one row [c | k_rope]: the d_c-wide latent c = x W_dkv[:, :d_c] and the
+ * d_rope-wide position key, rotated at the token's position before caching
+ * and shared by every head.  Keys and values are never materialised: the
+ * query of head h is folded into latent space (q_lat = W_uk_h q_nope), scored
+ * against the cached rows (q_lat . c + rot(q_rope) . k_rope), the softmax
+ * weights sum the latents into o_lat, and o_lat is projected out through
+ * W_uv_h.
+ *
+ * Sources (web pages, cited by title and section):
+ *   "Multi-head Latent Attention: the KV cache, compressed" (paperfordummies.in)
+ *     - "The one formula": what one cached row holds (d_c + d_rope elements).
+ *     - "Absorption: the part that makes it free": fold W_uk into the query
+ *       side once at load; keys are never built.
+ *     - "RoPE, and why the explanations stop here" and "The code"
+ *       (decoupled_score): the score is the absorbed content part plus a
+ *       rotated position part whose key is cached already rotated.
+ *   "Multi-head Latent Attention and KV Cache Compression" (jongkwan.dev),
+ *     "The absorption trick and decoupled RoPE": the value-side
+ *     up-projection folds onto the output side in the same way.
+ *   "Multi-Head Latent Attention (MLA)" (superteams.ai glossary), Hugging Face
+ *     config snippet: the field names of mla_config.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named "device" point to GPU memory the CALLER allocated and
+ *    owns (e.g. PyTorch tensors).  The library never allocates, frees or
+ *    retains device memory; it owns only the small host handle mla_layer.
+ *  - Every tensor is stored in cfg.dtype (fp32 or bf16, row-major, densely
+ *    packed) unless stated otherwise; index tensors are int32.  Arithmetic
+ *    accumulates in fp32; bf16 results are rounded to nearest even.
+ *  - Calls enqueue work on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and return without synchronising.  Faults inside kernels
+ *    surface at the caller's next synchronisation as HIP errors.
+ *  - Host-checkable problems (null pointers, non-positive sizes, odd d_rope,
+ *    unsupported shape/dtype, buffers too small) return a non-OK status
+ *    before anything is enqueued.  Values that live in device memory
+ *    (lengths, page ids) are trusted: the caller guarantees
+ *    1 <= q_len_b <= seq_len_b <= max_seq_len, q_len_b <= max_q_len and
+ *    that every page id a sequence touches lies in [0, num_pages).
+ *  - Positions are 0-based token indices.  Sequence b's cached token t lives
+ *    in row (t % page_size) of page page_table[b * max_pages + t / page_size].
+ *  - mla_last_error() returns a thread-local message for the last non-OK
+ *    status of the calling thread.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,            /* null pointer, bad size, inconsistent argument */
+  MLA_ERR_UNSUPPORTED = 2,            /* valid but not implemented (shape/dtype)      */
+  MLA_ERR_HIP = 3,                    /* a HIP runtime call failed                      */
+  MLA_ERR_INSUFFICIENT_WORKSPACE = 4  /* workspace or folded buffer too small           */
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* Shape of one MLA layer.  Field names follow the Hugging Face DeepSeek-V2
+ * config.  bf16 layers need kv_lora_rank == 512, qk_rope_head_dim == 64,
+ * qk_nope_head_dim and v_head_dim multiples of 32 and d_model a multiple of
+ * 256 (the matrix-core path); fp32 layers accept any positive sizes with an
+ * even qk_rope_head_dim. */
+typedef struct {
+  int32_t d_model;              /* hidden size of the tokens appended          */
+  int32_t num_attention_heads;  /* H                                           */
+  int32_t qk_nope_head_dim;     /* d_nope: content part of one head's query     */
+  int32_t qk_rope_head_dim;     /* d_rope: rotated part (even); cached once     */
+  int32_t v_head_dim;           /* d_v: output width per head                  */
+  int32_t kv_lora_rank;         /* d_c: latent width                           */
+  int32_t page_size;            /* tokens per cache page; multiple of 64       */
+  float rope_base;              /* rotary base, e.g. 10000                     */
+  float softmax_scale;          /* <= 0 selects 1/sqrt(d_nope + d_rope)         */
+  mla_dtype dtype;              /* storage dtype of every tensor               */
+} mla_config;
+
+typedef struct mla_layer mla_layer; /* opaque host handle */
+
+/* Bytes of the folded-weight buffer mla_fold_weights fills (0 if cfg is
+ * invalid or unsupported). */
+size_t mla_folded_bytes(const mla_config* cfg);
+
+/* Fold the layer's weights once at load ("Absorption: the part that makes it
+ * free": the fold happens once, not per step; rebuilding it in the decode
+ * loop is the tax shown under "Now break it").
+ *
+ *   w_dkv [d_model][d_c + d_rope]   device; columns d_c.. produce k_rope
+ *   w_uk  [d_c][H * d_nope]         device; head h = columns h*d_nope ..
+ *   w_uv  [d_c][H * d_v]            device; head h = columns h*d_v ..
+ *   folded                          device, >= mla_folded_bytes(cfg) bytes,
+ *                                   must stay alive and unchanged while the
+ *                                   layer is used; 256-byte aligned.
+ * The three weights are read by work enqueued on hip_stream and may be freed
+ * once that work has completed.  On success *out receives a new handle
+ * (release with mla_layer_free).  Errors: INVALID_ARG (null, bad sizes),
+ * UNSUPPORTED (shape/dtype), INSUFFICIENT_WORKSPACE (folded too small), HIP. */
+mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void* w_uk,
+                            const void* w_uv, void* folded, size_t folded_bytes,
+                            void* hip_stream, mla_layer** out);
+
+void mla_layer_free(mla_layer* layer);
+
+/* Bytes one token occupies in the cache: (d_c + d_rope) * sizeof(dtype)
+ * ("The one formula": one latent plus one position key per token and layer,
+ * independent of the head count).  0 if cfg is invalid. */
+size_t mla_cache_bytes_per_token(const mla_config* cfg);
+
+/* Workspace mla_append_latent needs for total_new new tokens. */
+size_t mla_append_workspace_bytes(const mla_layer* layer, int32_t total_new);
+
+/* Compute and cache the rows of new tokens ("The code": latent = x W_dkv is
+ * the only thing cached; decoupled_score: the rope key is stored already
+ * rotated, one copy for all heads).
+ *
+ *   x            [total_new][d_model]  device; tokens of sequence b are rows
+ *                                      cu_new[b] .. cu_new[b+1]-1
+ *   cu_new       [batch+1] int32       device; cu_new[0] = 0, nondecreasing,
+ *                                      cu_new[batch] = total_new
+ *   prefix_lens  [batch]   int32       device; tokens already cached; new token
+ *                                      j of b goes to position prefix_lens[b]+j
+ *   page_table   [batch][max_pages]    device int32
+ *   cache        [num_pages][page_size][d_c + d_rope]  device, updated in place
+ *   workspace    device, >= mla_append_workspace_bytes(layer, total_new)
+ * Row of a new token: u = x W_dkv (fp32 accumulation), c = u[:d_c],
+ * k_rope = rotate(u[d_c:], position); both rounded to dtype.  Only the rows
+ * of the new tokens are written.  total_new == 0 is a no-op. */
+mla_status mla_append_latent(const mla_layer* layer, const void* x, const int32_t* cu_new,
+                             const int32_t* prefix_lens, const int32_t* page_table,
+                             int32_t max_pages, int32_t batch, int32_t total_new, void* cache,
+                             int64_t num_pages, void* workspace, size_t workspace_bytes,
+                             void* hip_stream);
+
+/* Tokens of cache each split-KV work item covers for these bounds
+ * (kv_chunk > 0 is validated and returned; 0 picks a value from the batch
+ * size, the longest sequence and the GPU's compute-unit count).  Returns -1
+ * on invalid arguments. */
+int32_t mla_decode_kv_chunk(const mla_layer* layer, int32_t batch, int32_t max_q_len,
+                            int32_t max_seq_len, int32_t kv_chunk);
+
+/* Workspace mla_decode needs for these bounds (same kv_chunk meaning). */
+size_t mla_decode_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
+                                  int32_t max_q_len, int32_t max_seq_len, int32_t kv_chunk);
+
+/* One absorbed decode step over a paged latent cache.
+ *
+ *   q         [total_q][H][d_nope + d_rope]  device; queries BEFORE rotation;
+ *             sequence b owns rows cu_q[b] .. cu_q[b+1]-1
+ *   cu_q      [batch+1] int32 device (as cu_new)
+ *   seq_lens  [batch] int32 device; cached tokens of b INCLUDING its queries'
+ *             own rows (append first).  Query i of b sits at position
+ *             seq_lens[b] - q_len_b + i and attends to every position <= it.
+ *   page_table, cache   as for mla_append_latent (cache read only)
+ *   out       [total_q][H][d_v] device: out = softmax(score) V per head,
+ *             computed as (sum_t w_t c_t) W_uv_h; no output projection.
+ *   kv_chunk  tokens per split-KV work item, multiple of 64, or 0 (auto).
+ *             The split plan depends only on host arguments, so results are
+ *             run-to-run deterministic.
+ *   workspace device, >= mla_decode_workspace_bytes(...) bytes
+ * Errors: INVALID_ARG, UNSUPPORTED, INSUFFICIENT_WORKSPACE, HIP. */
+mla_status mla_decode(const mla_layer* layer, const void* q, const int32_t* cu_q,
+                      const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                      int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                      int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* The three phases of mla_decode, for callers that interleave their own
+ * work between them (timing, other streams):
+ *   MLA_PHASE_ABSORB  fold each query into latent space and rotate its rope
+ *                     part (writes the score operand into the workspace);
+ *   MLA_PHASE_ATTEND  split-KV attention over the cache (writes per-split
+ *                     partial outputs and log-sum-exps into the workspace);
+ *   MLA_PHASE_OUTPUT  merge the splits and project through W_uv into out.
+ * mla_decode_phases with the same arguments and workspace, called with the
+ * phases in this order (any grouping), is exactly mla_decode; `phases` is a
+ * nonzero OR of the flags.  The workspace carries the intermediate results
+ * from one call to the next and must not be modified in between. */
+typedef enum {
+  MLA_PHASE_ABSORB = 1,
+  MLA_PHASE_ATTEND = 2,
+  MLA_PHASE_OUTPUT = 4,
+  MLA_PHASE_ALL = 7
+} mla_decode_phase;
+
+mla_status mla_decode_phases(const mla_layer* layer, const void* q, const int32_t* cu_q,
+                             const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                             int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                             int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             uint32_t phases);
+
+const char* mla_status_string(mla_status s);
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

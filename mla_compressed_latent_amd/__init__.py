@@ -1,0 +1,249 @@
+"""Python binding of the MLA decode library (libmla.so, HIP for gfx950).
+
+A thin ctypes layer over the C ABI in ``include/mla.h``: each function has
+the C call's name, checks that the tensors it is handed are device-resident,
+contiguous and of the layer's dtype, and passes raw pointers.  All arithmetic
+runs in the library's kernels; PyTorch only supplies device memory and the
+current stream.  Importing this package fails loudly when libmla.so is
+missing -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MlaError", "MlaConfig", "Layer", "LIB_PATH", "lib",
+    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
+    "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
+    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
+    "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
+    "MLA_PHASE_ALL",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_INSUFFICIENT_WORKSPACE = range(5)
+MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
+MLA_PHASE_ABSORB, MLA_PHASE_ATTEND, MLA_PHASE_OUTPUT, MLA_PHASE_ALL = 1, 2, 4, 7
+
+EXPORTED_SYMBOLS = (
+    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
+    "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
+    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)}: {detail}")
+
+
+class MlaConfig(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32),
+        ("num_attention_heads", ctypes.c_int32),
+        ("qk_nope_head_dim", ctypes.c_int32),
+        ("qk_rope_head_dim", ctypes.c_int32),
+        ("v_head_dim", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == MLA_DTYPE_BF16 else torch.float32
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python mla_compressed_latent_amd/build.py` "
+            "(the decode path has no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    cfgp = ctypes.POINTER(MlaConfig)
+    sig = {
+        "mla_folded_bytes": (S, [cfgp]),
+        "mla_fold_weights": (I32, [cfgp, P, P, P, P, S, P, ctypes.POINTER(P)]),
+        "mla_layer_free": (None, [P]),
+        "mla_cache_bytes_per_token": (S, [cfgp]),
+        "mla_append_workspace_bytes": (S, [P, I32]),
+        "mla_append_latent": (I32, [P, P, P, P, P, I32, I32, I32, P, I64, P, S, P]),
+        "mla_decode_kv_chunk": (I32, [P, I32, I32, I32, I32]),
+        "mla_decode_workspace_bytes": (S, [P, I32, I32, I32, I32, I32]),
+        "mla_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
+        "mla_decode_phases": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P,
+                                    ctypes.c_uint32]),
+        "mla_status_string": (ctypes.c_char_p, [I32]),
+        "mla_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return lib.mla_status_string(s).decode()
+
+
+def mla_status_string(s: int) -> str:
+    return _status_name(s)
+
+
+def mla_last_error() -> str:
+    return lib.mla_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MlaError(status, where, mla_last_error())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def config_from_shape(shape, softmax_scale: float = 0.0) -> MlaConfig:
+    """MlaConfig from an object with the Hugging Face field names."""
+    return MlaConfig(
+        d_model=shape.d_model,
+        num_attention_heads=shape.num_attention_heads,
+        qk_nope_head_dim=shape.qk_nope_head_dim,
+        qk_rope_head_dim=shape.qk_rope_head_dim,
+        v_head_dim=shape.v_head_dim,
+        kv_lora_rank=shape.kv_lora_rank,
+        page_size=shape.page_size,
+        rope_base=float(shape.rope_base),
+        softmax_scale=float(softmax_scale),
+        dtype=MLA_DTYPE_BF16 if shape.dtype == "bf16" else MLA_DTYPE_F32,
+    )
+
+
+class Layer:
+    """Host handle of a folded layer; keeps the folded device buffer alive."""
+
+    def __init__(self, handle: ctypes.c_void_p, cfg: MlaConfig, folded: torch.Tensor):
+        self.handle = handle
+        self.cfg = cfg
+        self.folded = folded
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            lib.mla_layer_free(h)
+            self.handle = None
+
+
+def mla_folded_bytes(cfg: MlaConfig) -> int:
+    return int(lib.mla_folded_bytes(ctypes.byref(cfg)))
+
+
+def mla_cache_bytes_per_token(cfg: MlaConfig) -> int:
+    return int(lib.mla_cache_bytes_per_token(ctypes.byref(cfg)))
+
+
+def mla_fold_weights(cfg: MlaConfig, w_dkv, w_uk, w_uv, folded=None, stream=None) -> Layer:
+    dt = cfg.torch_dtype
+    n = mla_folded_bytes(cfg)
+    if n == 0:
+        # let the library report why
+        _check(lib.mla_fold_weights(ctypes.byref(cfg), None, None, None, None, 0, None,
+                                    ctypes.byref(ctypes.c_void_p())), "mla_fold_weights")
+    if folded is None:
+        folded = torch.empty(n, dtype=torch.uint8, device=w_dkv.device)
+    handle = ctypes.c_void_p()
+    _check(lib.mla_fold_weights(ctypes.byref(cfg), _dev(w_dkv, "w_dkv", dt), _dev(w_uk, "w_uk", dt),
+                                _dev(w_uv, "w_uv", dt), _dev(folded, "folded"), folded.numel() * folded.element_size(),
+                                _stream(stream), ctypes.byref(handle)), "mla_fold_weights")
+    return Layer(handle, cfg, folded)
+
+
+def mla_layer_free(layer: Layer):
+    if layer.handle:
+        lib.mla_layer_free(layer.handle)
+        layer.handle = None
+
+
+def mla_append_workspace_bytes(layer: Layer, total_new: int) -> int:
+    return int(lib.mla_append_workspace_bytes(layer.handle, int(total_new)))
+
+
+def mla_append_latent(layer: Layer, x, cu_new, prefix_lens, page_table, cache, workspace=None,
+                      stream=None):
+    """Append the rows of x ([total_new][d_model]) at positions prefix_lens[b] + j."""
+    dt = layer.cfg.torch_dtype
+    total_new = int(x.shape[0])
+    batch = int(prefix_lens.shape[0])
+    if workspace is None:
+        workspace = torch.empty(max(1, mla_append_workspace_bytes(layer, total_new)), dtype=torch.uint8,
+                                device=x.device)
+    _check(lib.mla_append_latent(
+        layer.handle, _dev(x, "x", dt), _dev(cu_new, "cu_new", torch.int32),
+        _dev(prefix_lens, "prefix_lens", torch.int32), _dev(page_table, "page_table", torch.int32),
+        int(page_table.shape[1]), batch, total_new, _dev(cache, "cache", dt), int(cache.shape[0]),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "mla_append_latent")
+
+
+def mla_decode_kv_chunk(layer: Layer, batch: int, max_q_len: int, max_seq_len: int, kv_chunk: int = 0) -> int:
+    return int(lib.mla_decode_kv_chunk(layer.handle, batch, max_q_len, max_seq_len, kv_chunk))
+
+
+def mla_decode_workspace_bytes(layer: Layer, batch: int, total_q: int, max_q_len: int, max_seq_len: int,
+                               kv_chunk: int = 0) -> int:
+    return int(lib.mla_decode_workspace_bytes(layer.handle, batch, total_q, max_q_len, max_seq_len, kv_chunk))
+
+
+def mla_decode(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_len: int, max_seq_len: int,
+               kv_chunk: int = 0, workspace=None, stream=None):
+    """out[t][h] = attention of query t, head h over its sequence's cached rows."""
+    return mla_decode_phases(layer, q, cu_q, seq_lens, page_table, cache, out, max_q_len, max_seq_len,
+                             kv_chunk, workspace, stream, MLA_PHASE_ALL)
+
+
+def mla_decode_phases(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_len: int,
+                      max_seq_len: int, kv_chunk: int = 0, workspace=None, stream=None,
+                      phases: int = MLA_PHASE_ALL):
+    """Run the selected phases of mla_decode (see include/mla.h)."""
+    dt = layer.cfg.torch_dtype
+    total_q = int(q.shape[0])
+    batch = int(seq_lens.shape[0])
+    if workspace is None:
+        if phases != MLA_PHASE_ALL:
+            raise ValueError("a partial phase mask needs the caller's workspace")
+        n = mla_decode_workspace_bytes(layer, batch, total_q, max_q_len, max_seq_len, kv_chunk)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_phases(
+        layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
+        int(max_seq_len), int(kv_chunk), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
+        int(phases)), "mla_decode")

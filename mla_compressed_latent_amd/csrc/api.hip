@@ -1,0 +1,324 @@
+// Host side of the C ABI declared in include/mla.h: argument validation,
+// buffer carving, the split plan, and kernel launches.  No device memory is
+// allocated here; every buffer comes from the caller.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mla.h"
+#include "kernels.hpp"
+
+struct mla_layer {
+  mla_config cfg;
+  int elem;        // bytes per stored element
+  float scale;     // softmax scale actually used
+  void* wdkv_t;    // [D][d_model]
+  void* wuk_p;     // [H][d_c][d_nope]
+  void* wuv_p;     // [H][d_v][d_c]
+  int num_cus;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+mla_status fail(mla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Checks a config; returns MLA_OK or the failing status (message in g_err).
+mla_status check_config(const mla_config* c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARG, "config is null");
+  if (c->d_model <= 0 || c->num_attention_heads <= 0 || c->qk_nope_head_dim <= 0 ||
+      c->qk_rope_head_dim <= 0 || c->v_head_dim <= 0 || c->kv_lora_rank <= 0 || c->page_size <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "every dimension must be positive");
+  if (c->qk_rope_head_dim % 2) return fail(MLA_ERR_INVALID_ARG, "qk_rope_head_dim must be even");
+  if (c->kv_lora_rank % 2) return fail(MLA_ERR_INVALID_ARG, "kv_lora_rank must be even");
+  if (c->page_size % 64) return fail(MLA_ERR_INVALID_ARG, "page_size must be a multiple of 64");
+  if (!(c->rope_base > 1.f) || !isfinite(c->rope_base))
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be a finite value > 1");
+  if (!isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (c->dtype == MLA_DTYPE_BF16) {
+    if (c->kv_lora_rank != 512 || c->qk_rope_head_dim != 64)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need kv_lora_rank 512 and qk_rope_head_dim 64");
+    if (c->qk_nope_head_dim % 32 || c->v_head_dim % 32)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need qk_nope_head_dim, v_head_dim multiples of 32");
+    if (c->d_model % 256)
+      return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need d_model to be a multiple of 256");
+  } else if (c->dtype == MLA_DTYPE_F32) {
+    if (c->kv_lora_rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "fp32 layers need kv_lora_rank <= 1024");
+  } else {
+    return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
+  }
+  return MLA_OK;
+}
+
+int elem_of(const mla_config* c) { return c->dtype == MLA_DTYPE_BF16 ? 2 : 4; }
+
+struct FoldLayout {
+  size_t off_wdkv, off_wuk, off_wuv, total;
+};
+
+FoldLayout fold_layout(const mla_config* c) {
+  const size_t e = elem_of(c);
+  const size_t D = (size_t)c->kv_lora_rank + c->qk_rope_head_dim;
+  FoldLayout f;
+  f.off_wdkv = 0;
+  f.off_wuk = align256(D * c->d_model * e);
+  f.off_wuv = f.off_wuk + align256((size_t)c->num_attention_heads * c->kv_lora_rank * c->qk_nope_head_dim * e);
+  f.total = f.off_wuv + align256((size_t)c->num_attention_heads * c->v_head_dim * c->kv_lora_rank * e);
+  return f;
+}
+
+mla_status hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+// Split plan for a decode call (depends on host arguments only).
+bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, int kv_chunk,
+               mla::SplitPlan* p) {
+  const int H = L->cfg.num_attention_heads;
+  const int rows = max_q_len * H;
+  if (L->elem == 2) {
+    if (rows > 32) { p->NB = 2; p->RQ = (rows + 63) / 64; }
+    else { p->NB = 1; p->RQ = 1; }
+  } else {
+    p->NB = 1;
+    p->RQ = 1;
+  }
+  if (kv_chunk > 0) {
+    if (kv_chunk % 64) return false;
+    p->chunk = kv_chunk;
+  } else {
+    // One resident workgroup per compute unit (two when the row block is
+    // small); cover the longest sequences with about one wave of workgroups,
+    // capped so ragged batches still balance.
+    const int per_cu = 1;
+    const double target = (double)L->num_cus * per_cu;
+    const double work = (double)batch * p->RQ * max_seq_len;
+    long c = (long)ceil(work / target);
+    c = ((c + 63) / 64) * 64;
+    if (c < 256) c = 256;
+    if (c > 4096) c = 4096;
+    p->chunk = (int)c;
+  }
+  p->S_max = (max_seq_len + p->chunk - 1) / p->chunk;
+  return true;
+}
+
+struct DecodeLayout {
+  size_t off_abuf, off_opart, off_lse, off_olat, total;
+};
+
+DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan& p) {
+  const mla_config& c = L->cfg;
+  const size_t rows = (size_t)total_q * c.num_attention_heads;
+  const size_t D = (size_t)c.kv_lora_rank + c.qk_rope_head_dim;
+  DecodeLayout d;
+  d.off_abuf = 0;
+  d.off_opart = align256(rows * D * L->elem);
+  d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * 4);
+  d.off_olat = d.off_lse + align256((size_t)p.S_max * rows * 4);
+  d.total = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
+  return d;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_INSUFFICIENT_WORKSPACE: return "MLA_ERR_INSUFFICIENT_WORKSPACE";
+  }
+  return "unknown mla_status";
+}
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+size_t mla_folded_bytes(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return fold_layout(cfg).total;
+}
+
+size_t mla_cache_bytes_per_token(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return (size_t)(cfg->kv_lora_rank + cfg->qk_rope_head_dim) * elem_of(cfg);
+}
+
+mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void* w_uk,
+                            const void* w_uv, void* folded, size_t folded_bytes, void* hip_stream,
+                            mla_layer** out) {
+  mla_status st = check_config(cfg);
+  if (st != MLA_OK) return st;
+  if (!w_dkv || !w_uk || !w_uv || !folded || !out)
+    return fail(MLA_ERR_INVALID_ARG, "mla_fold_weights: null pointer argument");
+  if ((uintptr_t)folded % 256) return fail(MLA_ERR_INVALID_ARG, "folded buffer must be 256-byte aligned");
+  const FoldLayout f = fold_layout(cfg);
+  if (folded_bytes < f.total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "folded buffer holds %zu bytes, %zu needed", folded_bytes,
+                f.total);
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    return fail(MLA_ERR_HIP, "cannot query the current device");
+  mla_layer* L = new mla_layer;
+  L->cfg = *cfg;
+  L->elem = elem_of(cfg);
+  L->scale = cfg->softmax_scale > 0.f
+                 ? cfg->softmax_scale
+                 : (float)(1.0 / sqrt((double)(cfg->qk_nope_head_dim + cfg->qk_rope_head_dim)));
+  L->wdkv_t = (char*)folded + f.off_wdkv;
+  L->wuk_p = (char*)folded + f.off_wuk;
+  L->wuv_p = (char*)folded + f.off_wuv;
+  L->num_cus = ncu;
+  mla::launch_pack(L->elem, w_dkv, w_uk, w_uv, L->wdkv_t, L->wuk_p, L->wuv_p, cfg->d_model,
+                   cfg->num_attention_heads, cfg->qk_nope_head_dim, cfg->v_head_dim,
+                   cfg->kv_lora_rank, cfg->qk_rope_head_dim, (hipStream_t)hip_stream);
+  st = hip_check("fold launch");
+  if (st != MLA_OK) {
+    delete L;
+    return st;
+  }
+  *out = L;
+  return MLA_OK;
+}
+
+void mla_layer_free(mla_layer* layer) { delete layer; }
+
+size_t mla_append_workspace_bytes(const mla_layer* L, int32_t total_new) {
+  if (!L || total_new < 0) return 0;
+  const size_t D = (size_t)L->cfg.kv_lora_rank + L->cfg.qk_rope_head_dim;
+  const size_t ks = L->elem == 2 ? (size_t)mla::append_ksplits_bf16(L->cfg.d_model) : 1;
+  return align256(ks * (size_t)total_new * D * 4);
+}
+
+mla_status mla_append_latent(const mla_layer* L, const void* x, const int32_t* cu_new,
+                             const int32_t* prefix_lens, const int32_t* page_table, int32_t max_pages,
+                             int32_t batch, int32_t total_new, void* cache, int64_t num_pages,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (total_new < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_latent: bad sizes (batch %d, total_new %d, max_pages %d)",
+                batch, total_new, max_pages);
+  if (total_new == 0) return MLA_OK;
+  if (!x || !cu_new || !prefix_lens || !page_table || !cache || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_append_latent: null pointer argument");
+  const size_t need = mla_append_workspace_bytes(L, total_new);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "append workspace holds %zu bytes, %zu needed",
+                workspace_bytes, need);
+  const mla_config& c = L->cfg;
+  const int D = c.kv_lora_rank + c.qk_rope_head_dim;
+  hipStream_t st = (hipStream_t)hip_stream;
+  float* part = (float*)workspace;
+  int ks = 1;
+  if (L->elem == 2) {
+    ks = mla::append_ksplits_bf16(c.d_model);
+    mla::launch_append_gemm_bf16(x, L->wdkv_t, part, total_new, D, c.d_model, st);
+  } else {
+    mla::launch_append_gemm_f32(x, L->wdkv_t, part, total_new, D, c.d_model, st);
+  }
+  mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
+                            batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
+                            st);
+  return hip_check("append launch");
+}
+
+int32_t mla_decode_kv_chunk(const mla_layer* L, int32_t batch, int32_t max_q_len, int32_t max_seq_len,
+                            int32_t kv_chunk) {
+  if (!L || batch <= 0 || max_q_len <= 0 || max_seq_len < max_q_len || kv_chunk < 0) return -1;
+  mla::SplitPlan p;
+  if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p)) return -1;
+  return p.chunk;
+}
+
+size_t mla_decode_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_q, int32_t max_q_len,
+                                  int32_t max_seq_len, int32_t kv_chunk) {
+  if (!L || batch <= 0 || total_q <= 0 || max_q_len <= 0 || max_seq_len < max_q_len || kv_chunk < 0)
+    return 0;
+  mla::SplitPlan p;
+  if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p)) return 0;
+  return decode_layout(L, total_q, p).total;
+}
+
+mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* cu_q,
+                             const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                             int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                             int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             uint32_t phases) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (phases == 0 || (phases & ~(uint32_t)MLA_PHASE_ALL))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_phases: bad phase mask 0x%x", phases);
+  if (!q || !cu_q || !seq_lens || !page_table || !cache || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer argument");
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len || max_pages <= 0 ||
+      num_pages <= 0 || (int64_t)max_pages * L->cfg.page_size < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_decode: bad sizes (batch %d, total_q %d, max_q_len %d, max_seq_len %d, max_pages %d)",
+                batch, total_q, max_q_len, max_seq_len, max_pages);
+  if ((int64_t)total_q > (int64_t)batch * max_q_len)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: total_q exceeds batch * max_q_len");
+  if (kv_chunk < 0 || kv_chunk % 64)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a positive multiple of 64");
+  mla::SplitPlan p;
+  if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: cannot plan the split");
+  const DecodeLayout d = decode_layout(L, total_q, p);
+  if (workspace_bytes < d.total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "decode workspace holds %zu bytes, %zu needed",
+                workspace_bytes, d.total);
+  if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const mla_config& c = L->cfg;
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  void* abuf = ws + d.off_abuf;
+  float* opart = (float*)(ws + d.off_opart);
+  float* lse = (float*)(ws + d.off_lse);
+  void* olat = ws + d.off_olat;
+  const int H = c.num_attention_heads;
+  if (phases & MLA_PHASE_ABSORB)
+    mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, H, c.qk_nope_head_dim,
+                       c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, st);
+  if (phases & MLA_PHASE_ATTEND)
+    mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
+                        c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse, st);
+  if (phases & MLA_PHASE_OUTPUT) {
+    mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank, olat, st);
+    mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim, st);
+  }
+  return hip_check("decode launch");
+}
+
+mla_status mla_decode(const mla_layer* L, const void* q, const int32_t* cu_q, const int32_t* seq_lens,
+                      const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t total_q,
+                      int32_t max_q_len, int32_t max_seq_len, int32_t kv_chunk, const void* cache,
+                      int64_t num_pages, void* out, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  return mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                           max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
+                           hip_stream, MLA_PHASE_ALL);
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,129 @@
+// Append: compute the cached row of each new token and write it into its page.
+//
+// Row of token x at position p ("Multi-head Latent Attention: the KV cache,
+// compressed", sections "The one formula" and "The code": the latent
+// x W_dkv is the only thing cached; the decoupled rope key is cached already
+// rotated, one copy shared by all heads):
+//     u = x W_dkv                    (d_c + d_rope wide, fp32 accumulation)
+//     row = [ u[:d_c] | rot(u[d_c:], p) ]   rounded to the cache dtype
+//
+// The GEMM is split along d_model so that a handful of new tokens still
+// spreads over the whole chip; the split partials are summed in a fixed
+// order by the finishing kernel, so the cache contents are deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int kAppendKChunk = 256;   // d_model elements per split
+
+// One wave computes a 32 (tokens) x 32 (row elements) tile over one k chunk.
+__global__ __launch_bounds__(64) void append_gemm_bf16_kernel(const bf16* __restrict__ x,
+                                                              const bf16* __restrict__ wt,
+                                                              float* __restrict__ part, int M,
+                                                              int N, int K) {
+  const int lane = threadIdx.x;
+  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32, ks = blockIdx.z;
+  const int k0 = ks * kAppendKChunk + 8 * (lane >> 5);
+  const int mrow = min(m0 + (lane & 31), M - 1);
+  const bf16* xa = x + (int64_t)mrow * K + k0;
+  const bf16* wb = wt + (int64_t)(n0 + (lane & 31)) * K + k0;
+  bf16x8 a[kAppendKChunk / 16], b[kAppendKChunk / 16];
+#pragma unroll
+  for (int s = 0; s < kAppendKChunk / 16; ++s) {
+    a[s] = load_bf16x8(xa + 16 * s);
+    b[s] = load_bf16x8(wb + 16 * s);
+  }
+  f32x16 acc = zero_f32x16();
+#pragma unroll
+  for (int s = 0; s < kAppendKChunk / 16; ++s) acc = mfma32(a[s], b[s], acc);
+  float* out = part + (int64_t)ks * M * N;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    int m = m0 + acc_row32(r, lane);
+    if (m < M) out[(int64_t)m * N + n0 + (lane & 31)] = acc[r];
+  }
+}
+
+// fp32 layers: one thread per output element, sequential k order.
+__global__ void append_gemm_f32_kernel(const float* __restrict__ x, const float* __restrict__ wt,
+                                       float* __restrict__ part, int M, int N, int K) {
+  int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= (int64_t)M * N) return;
+  int m = (int)(o / N), n = (int)(o % N);
+  const float* xr = x + (int64_t)m * K;
+  const float* wr = wt + (int64_t)n * K;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc = fmaf(xr[k], wr[k], acc);
+  part[o] = acc;
+}
+
+template <typename T>
+__global__ void append_finish_kernel(const float* __restrict__ part, int ksplits, int T_new,
+                                     const int32_t* __restrict__ cu_new,
+                                     const int32_t* __restrict__ prefix_lens,
+                                     const int32_t* __restrict__ page_table, int max_pages,
+                                     int batch, T* __restrict__ cache, int page_size, int dc,
+                                     int dr, float base) {
+  const int t = blockIdx.x;
+  const int D = dc + dr;
+  const int b = seq_of_token(cu_new, batch, t);
+  const int pos = prefix_lens[b] + (t - cu_new[b]);
+  const int page = page_table[(int64_t)b * max_pages + pos / page_size];
+  T* dst = cache + ((int64_t)page * page_size + pos % page_size) * D;
+  const int64_t stride = (int64_t)T_new * D;
+  for (int p = threadIdx.x; p < D / 2; p += blockDim.x) {
+    const int n = 2 * p;
+    float u0 = 0.f, u1 = 0.f;
+    const float* src = part + (int64_t)t * D + n;
+    for (int ks = 0; ks < ksplits; ++ks) {
+      u0 += src[ks * stride];
+      u1 += src[ks * stride + 1];
+    }
+    if (n >= dc) {
+      float c, s;
+      rope_cos_sin(pos, (n - dc) >> 1, dr, base, &c, &s);
+      float r0 = u0 * c - u1 * s;
+      float r1 = u0 * s + u1 * c;
+      u0 = r0;
+      u1 = r1;
+    }
+    dst[n] = from_f32<T>(u0);
+    dst[n + 1] = from_f32<T>(u1);
+  }
+}
+
+}  // namespace
+
+int append_ksplits_bf16(int K) { return K / kAppendKChunk; }
+
+void launch_append_gemm_bf16(const void* x, const void* wt, float* part, int M, int N, int K,
+                             hipStream_t st) {
+  dim3 grid((M + 31) / 32, N / 32, K / kAppendKChunk);
+  append_gemm_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)x, (const bf16*)wt, part, M, N, K);
+}
+
+void launch_append_gemm_f32(const void* x, const void* wt, float* part, int M, int N, int K,
+                            hipStream_t st) {
+  int64_t n = (int64_t)M * N;
+  append_gemm_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const float*)x,
+                                                                      (const float*)wt, part, M,
+                                                                      N, K);
+}
+
+void launch_append_finish(int elem, const float* part, int ksplits, int T, const int32_t* cu_new,
+                          const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
+                          int batch, void* cache, int page_size, int dc, int dr, float base,
+                          hipStream_t st) {
+  if (elem == 2)
+    append_finish_kernel<bf16><<<T, 256, 0, st>>>(part, ksplits, T, cu_new, prefix_lens,
+                                                  page_table, max_pages, batch, (bf16*)cache,
+                                                  page_size, dc, dr, base);
+  else
+    append_finish_kernel<float><<<T, 256, 0, st>>>(part, ksplits, T, cu_new, prefix_lens,
+                                                   page_table, max_pages, batch, (float*)cache,
+                                                   page_size, dc, dr, base);
+}
+
+}  // namespace mla

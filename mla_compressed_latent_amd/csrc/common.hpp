@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the MLA decode kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ numbers
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// Rotary angle for pair i at position pos, computed in double:
+// theta_i = base^(-2i/d_rope), angle = pos * theta_i.  Long positions
+// (1e5 and more) need the double product and double sin/cos.
+__device__ __forceinline__ void rope_cos_sin(int pos, int pair, int d_rope, float base,
+                                             float* c, float* s) {
+  double theta = pow(static_cast<double>(base), -2.0 * pair / static_cast<double>(d_rope));
+  double ang = static_cast<double>(pos) * theta;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+// Index of the sequence that owns flat token t, given cu[0..batch] (cu[0]=0,
+// nondecreasing).  Largest b with cu[b] <= t.
+__device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int batch, int t) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- matrix core
+// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.
+// Lane l holds A row (l % 32) and B column (l % 32), eight consecutive k
+// values each; both operands use the same k assignment.  Accumulator
+// element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row32(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// XCD-aware block order: the hardware deals consecutive workgroup ids to the
+// 8 XCDs in turn; this maps them so that consecutive *logical* ids run on
+// the same XCD (and share its L2).
+__device__ __forceinline__ int xcd_logical_block(int id, int n) {
+  constexpr int kXcd = 8;
+  int per = (n + kXcd - 1) / kXcd;
+  int xcd = id % kXcd, local = id / kXcd;
+  // the last XCDs get fewer blocks when n is not a multiple of 8
+  int full = n - (per - 1) * kXcd;  // number of XCDs holding `per` blocks
+  int base = xcd < full ? xcd * per : full * per + (xcd - full) * (per - 1);
+  return base + local;
+}
+
+}  // namespace mla

@@ -1,0 +1,54 @@
+// Internal launchers of the MLA decode library (host side, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---- fold (pack) ---------------------------------------------------------
+// wdkv_t[n][d] = w_dkv[d][n]; wuk_p[h][j][i] = w_uk[j][h*dn+i];
+// wuv_p[h][v][j] = w_uv[j][h*dv+v].  elem = 2 (bf16) or 4 (fp32).
+void launch_pack(int elem, const void* w_dkv, const void* w_uk, const void* w_uv, void* wdkv_t,
+                 void* wuk_p, void* wuv_p, int d_model, int H, int dn, int dv, int dc, int dr,
+                 hipStream_t st);
+
+// ---- append --------------------------------------------------------------
+// part[ks][m][n] = sum over the ks-th k chunk of x[m][k] * wt[n][k].
+int append_ksplits_bf16(int K);
+void launch_append_gemm_bf16(const void* x, const void* wt, float* part, int M, int N, int K,
+                             hipStream_t st);
+void launch_append_gemm_f32(const void* x, const void* wt, float* part, int M, int N, int K,
+                            hipStream_t st);
+// Sum the k partials, rotate the rope block, round and scatter into pages.
+void launch_append_finish(int elem, const float* part, int ksplits, int T, const int32_t* cu_new,
+                          const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
+                          int batch, void* cache, int page_size, int dc, int dr, float base,
+                          hipStream_t st);
+
+// ---- per-head GEMMs --------------------------------------------------------
+// abuf[t][h][0:dc] = W_uk_h q_nope[t][h]; abuf[t][h][dc:] = rot(q_rope, pos_t)
+void launch_absorb(int elem, const void* q, const void* wuk_p, void* abuf, const int32_t* cu_q,
+                   const int32_t* seq_lens, int batch, int Tq, int H, int dn, int dr, int dc,
+                   float base, hipStream_t st);
+// out[t][h][v] = sum_j olat[t][h][j] * wuv_p[h][v][j]
+void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
+                     int dv, hipStream_t st);
+
+// ---- split-KV attention over the latent cache --------------------------------
+struct SplitPlan {
+  int chunk;    // tokens per work item (multiple of 64)
+  int S_max;    // splits of the longest sequence
+  int RQ;       // row groups per sequence (bf16 path)
+  int NB;       // 32-row blocks per workgroup (bf16 path)
+};
+void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
+                    const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
+                    int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
+                    float scale, float* opart, float* lse, hipStream_t st);
+// olat[t][h][:] = LSE-weighted merge of the split partials
+void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
+                    const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,
+                    void* olat, hipStream_t st);
+
+}  // namespace mla

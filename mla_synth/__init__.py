@@ -5,7 +5,10 @@ lays out lengths and page tables.  It holds none of the attention arithmetic:
 both the GPU library and the CPU oracle consume what it produces.
 """
 from .workloads import (  # noqa: F401
+    DSV2,
+    LLAMA2_7B_MLA,
     Shape,
+    TINY,
     Workload,
     WORKLOADS,
     workload,

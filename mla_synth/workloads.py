@@ -258,6 +258,6 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, **overrides) -> Workload:
-    wl = WORKLOADS[name]
+def workload(key: str, **overrides) -> Workload:
+    wl = WORKLOADS[key]
     return wl.with_(**overrides) if overrides else wl

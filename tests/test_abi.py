@@ -1,0 +1,101 @@
+"""The C ABI library: it loads, exports every function include/mla.h
+declares, and rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import mla_compressed_latent_amd as m
+    return m
+
+
+def test_header_and_exports_agree(mla):
+    declared = _declared()
+    assert set(declared) == set(mla.EXPORTED_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (mla_[a-z_]+)$", out, flags=re.M))
+    assert set(declared) <= exported, set(declared) - exported
+    assert exported <= set(declared), f"undeclared exports {exported - set(declared)}"
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def _cfg(mla, **kw):
+    base = dict(d_model=5120, num_attention_heads=128, qk_nope_head_dim=128, qk_rope_head_dim=64,
+                v_head_dim=128, kv_lora_rank=512, page_size=64, rope_base=10000.0, softmax_scale=0.0,
+                dtype=1)
+    base.update(kw)
+    return mla.MlaConfig(**base)
+
+
+def test_cache_bytes_per_token(mla):
+    # one latent plus one rope key per token, independent of the head count
+    assert mla.mla_cache_bytes_per_token(_cfg(mla)) == 576 * 2
+    assert mla.mla_cache_bytes_per_token(_cfg(mla, num_attention_heads=32, d_model=4096)) == 1152
+    tiny = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                v_head_dim=16, kv_lora_rank=32, dtype=0)
+    assert mla.mla_cache_bytes_per_token(tiny) == 40 * 4
+
+
+def test_folded_bytes_covers_packed_weights(mla):
+    n = mla.mla_folded_bytes(_cfg(mla))
+    w = (5120 * 576 + 512 * 128 * 128 * 2) * 2
+    assert w <= n < w + 3 * 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qk_rope_head_dim=63, dtype=0), 1),
+    (dict(page_size=48), 1),
+    (dict(num_attention_heads=0), 1),
+    (dict(dtype=7), 1),
+    (dict(kv_lora_rank=256), 2),          # bf16 path is built for d_c = 512
+    (dict(qk_rope_head_dim=32), 2),
+    (dict(d_model=5000), 2),
+])
+def test_config_rejections(mla, kw, status):
+    cfg = _cfg(mla, **kw)
+    assert mla.mla_folded_bytes(cfg) == 0
+    h = ctypes.c_void_p()
+    st = mla.lib.mla_fold_weights(ctypes.byref(cfg), ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                  ctypes.c_void_p(256), 1 << 40, None, ctypes.byref(h))
+    assert st == status, mla.mla_last_error()
+    assert mla.mla_last_error()
+
+
+def test_null_and_size_errors(mla):
+    cfg = _cfg(mla)
+    h = ctypes.c_void_p()
+    assert mla.lib.mla_fold_weights(ctypes.byref(cfg), None, None, None, None, 0, None, ctypes.byref(h)) == 1
+    assert "null" in mla.mla_last_error()
+    # misaligned folded buffer
+    assert mla.lib.mla_fold_weights(ctypes.byref(cfg), ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                    ctypes.c_void_p(8), 1 << 40, None, ctypes.byref(h)) == 1
+    # folded buffer too small
+    assert mla.lib.mla_fold_weights(ctypes.byref(cfg), ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                    ctypes.c_void_p(256), 1024, None, ctypes.byref(h)) == 4
+    # calls without a layer
+    assert mla.lib.mla_decode(None, *([None] * 4), 1, 1, 1, 1, 1, 0, None, 1, None, None, 0, None) == 1
+    assert mla.lib.mla_append_latent(None, *([None] * 4), 1, 1, 1, None, 1, None, 0, None) == 1
+    assert mla.lib.mla_decode_workspace_bytes(None, 1, 1, 1, 1, 0) == 0
+    assert mla.lib.mla_decode_kv_chunk(None, 1, 1, 1, 0) == -1
+
+
+def test_status_strings(mla):
+    assert [mla.mla_status_string(i) for i in range(5)] == [
+        "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_HIP", "MLA_ERR_INSUFFICIENT_WORKSPACE"]

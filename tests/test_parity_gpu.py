@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on
+the same seeded inputs.
+
+Tolerances: fp32 layers max|gpu - ref| / max|ref| <= 1e-4.  bf16 layers:
+with the outputs scaled to unit maximum the largest absolute error is <= 1e-2
+(max|gpu - ref| / max|ref| <= 1e-2, inside the 2e-2 maximum relative error),
+and the aggregate error rms(gpu - ref) / rms(ref) <= 1e-2.  The bf16 output
+is itself a rounding of the exact result (half an ulp is up to 2**-8 of an
+element), so no bound on single elements relative to the typical output
+magnitude can be tighter than a few times 2**-8."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mla_synth import DSV2, LLAMA2_7B_MLA, WORKLOADS, workload
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import GpuCase, errors, oracle_outputs  # noqa: E402
+
+F32_TOL = 1e-4
+BF16_REL_MAX = 1e-2
+BF16_REL_RMS = 1e-2
+
+
+def _check(case: GpuCase, out: torch.Tensor, seqs=None, heads=None, tag=""):
+    wl = case.wl
+    got = out.float().cpu().numpy()
+    cu = wl.cu_q()
+    seqs = range(wl.batch) if seqs is None else seqs
+    worst = (0.0, 0.0, 0.0)
+    bf16 = wl.shape.dtype != "f32"
+    for b in seqs:
+        ref = oracle_outputs(wl, b, heads, case.w_dkv, case.w_uk, case.w_uv)
+        g = got[cu[b]:cu[b + 1]]
+        if heads is not None:
+            g = g[:, heads]
+        e = errors(g, ref)
+        worst = tuple(max(x, y) for x, y in zip(worst, e))
+        if not bf16:
+            assert e[0] <= F32_TOL, f"{tag} seq {b}: rel err {e[0]:.3e}"
+        else:
+            assert e[0] <= BF16_REL_MAX and e[1] <= BF16_REL_RMS, f"{tag} seq {b}: errors {e}"
+    print(f"[parity] {tag}: max|d|/max|ref| {worst[0]:.3e}, rms(d)/rms(ref) {worst[1]:.3e}, "
+          f"max|d|/rms(ref) {worst[2]:.3e}", flush=True)
+    return worst
+
+
+def _run(wl, kv_chunk=0, **kw):
+    print(f"[parity] case {wl.name} B={wl.batch} kv_chunk={kv_chunk}", flush=True)
+    case = GpuCase(wl)
+    case.append_new()
+    out = case.decode(kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    return case, out
+
+
+def test_tiny_fp32_full():
+    wl = WORKLOADS["tiny_f32"]
+    case, out = _run(wl)
+    _check(case, out, tag="tiny_f32")
+
+
+def test_tiny_fp32_ragged_paged():
+    wl = WORKLOADS["tiny_f32"].with_(name="tiny_f32_ragged", batch=5, fixed_prefix=None, max_prefix=300,
+                                     fixed_q_len=None, max_q_len=2, paging="random", spare_page_frac=0.3)
+    case, out = _run(wl, kv_chunk=64)
+    _check(case, out, tag="tiny_f32_ragged")
+
+
+SMALL_DSV2 = dataclasses.replace(DSV2, d_model=512)
+SMALL_LLAMA = dataclasses.replace(LLAMA2_7B_MLA, d_model=512)
+
+
+@pytest.mark.parametrize("kv_chunk", [0, 64, 192])
+def test_bf16_dsv2_hidden_prefix(kv_chunk):
+    wl = workload("dsv2_b32_ctx4096", name="dsv2_small", shape=SMALL_DSV2, batch=3, fixed_prefix=None,
+                  max_prefix=700)
+    case, out = _run(wl, kv_chunk=kv_chunk)
+    _check(case, out, tag=f"dsv2_small chunk={kv_chunk}")
+
+
+def test_bf16_dsv2_ragged_paged_two_queries():
+    wl = workload("dsv2_ragged_paged_256", name="dsv2_ragged_small", batch=7, max_prefix=400)
+    case, out = _run(wl, kv_chunk=128)
+    _check(case, out, tag="dsv2_ragged_small")
+
+
+def test_bf16_llama_shape():
+    wl = workload("llama2_7b_mla_b64_ctx8192", name="llama_small", shape=SMALL_LLAMA, batch=4,
+                  fixed_prefix=None, max_prefix=900)
+    case, out = _run(wl)
+    _check(case, out, tag="llama_small")
+
+
+def test_bf16_llama_two_queries_paged():
+    wl = workload("llama2_7b_mla_b64_ctx8192", name="llama_q2", shape=SMALL_LLAMA, batch=5,
+                  fixed_prefix=None, max_prefix=500, fixed_q_len=None, max_q_len=2, paging="random",
+                  spare_page_frac=0.1)
+    case, out = _run(wl, kv_chunk=256)
+    _check(case, out, tag="llama_q2")
+
+
+def test_minimal_contexts():
+    """Context 1 (one query on its own row) and context 2 with two queries."""
+    for q_len in (1, 2):
+        wl = workload("dsv2_ragged_paged_256", name=f"minimal_q{q_len}", batch=2, fixed_prefix=0,
+                      fixed_q_len=q_len)
+        case, out = _run(wl)
+        _check(case, out, tag=f"minimal q_len={q_len}")
+
+
+def test_deterministic_and_page_permutation_invariant():
+    wl = workload("dsv2_ragged_paged_256", name="perm", batch=4, max_prefix=300)
+    case, out1 = _run(wl, kv_chunk=128)
+    out2 = case.decode(kv_chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "two runs differ"
+    # same logical cache, different physical pages (different seed for the permutation)
+    wl2 = wl.with_(seed=wl.seed)  # same data
+    case2 = GpuCase(wl2)
+    perm = np.random.default_rng(99).permutation(case2.num_pages).astype(np.int32)
+    new_table = np.where(case2.table_np >= 0, perm[np.maximum(case2.table_np, 0)], -1).astype(np.int32)
+    src = torch.from_numpy(case2.table_np[case2.table_np >= 0].astype(np.int64)).cuda()
+    dst = torch.from_numpy(new_table[case2.table_np >= 0].astype(np.int64)).cuda()
+    moved = case2.cache.clone()
+    moved[dst] = case2.cache[src]
+    case2.cache = moved
+    case2.table_np = new_table
+    case2.page_table = torch.from_numpy(new_table).cuda()
+    case2.append_new()
+    out3 = case2.decode(kv_chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out3), "page permutation changed the result"
+
+
+def test_split_invariance():
+    wl = workload("dsv2_b32_ctx4096", name="splits", shape=SMALL_DSV2, batch=2, fixed_prefix=1000)
+    case, out_a = _run(wl, kv_chunk=64)
+    out_b = case.decode(kv_chunk=1024)
+    out_c = case.decode(kv_chunk=0)
+    torch.cuda.synchronize()
+    a, b, c = (o.float().cpu().numpy() for o in (out_a, out_b, out_c))
+    scale = np.abs(a).max()
+    assert np.abs(a - b).max() / scale < 1e-2 and np.abs(a - c).max() / scale < 1e-2
