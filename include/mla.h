@@ -70,8 +70,9 @@ typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
 /* Shape of one MLA layer.  Field names follow the Hugging Face DeepSeek-V2
  * config.  bf16 layers need kv_lora_rank == 512, qk_rope_head_dim == 64,
  * qk_nope_head_dim and v_head_dim multiples of 32 and d_model a multiple of
- * 256 (the matrix-core path); fp32 layers accept any positive sizes with an
- * even qk_rope_head_dim. */
+ * 256 (the matrix-core path); fp32 layers accept positive sizes with an
+ * even qk_rope_head_dim and a kv_lora_rank that is a multiple of 4, at most
+ * 1024. */
 typedef struct {
   int32_t d_model;              /* hidden size of the tokens appended          */
   int32_t num_attention_heads;  /* H                                           */
@@ -163,7 +164,8 @@ size_t mla_decode_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t
  *   page_table, cache   as for mla_append_latent (cache read only)
  *   out       [total_q][H][d_v] device: out = softmax(score) V per head,
  *             computed as (sum_t w_t c_t) W_uv_h; no output projection.
- *   kv_chunk  tokens per split-KV work item, multiple of 64, or 0 (auto).
+ *   kv_chunk  tokens per split-KV work item, a multiple of 64 up to 8192, or
+ *             0 (auto); at most 1024 splits per sequence.
  *             The split plan depends only on host arguments, so results are
  *             run-to-run deterministic.
  *   workspace device, >= mla_decode_workspace_bytes(...) bytes

@@ -58,7 +58,8 @@ mla_status check_config(const mla_config* c) {
     if (c->d_model % 256)
       return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need d_model to be a multiple of 256");
   } else if (c->dtype == MLA_DTYPE_F32) {
-    if (c->kv_lora_rank > 1024) return fail(MLA_ERR_UNSUPPORTED, "fp32 layers need kv_lora_rank <= 1024");
+    if (c->kv_lora_rank > 1024 || c->kv_lora_rank % 4)
+      return fail(MLA_ERR_UNSUPPORTED, "fp32 layers need kv_lora_rank <= 1024 and a multiple of 4");
   } else {
     return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
   }
@@ -94,14 +95,15 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
   const int H = L->cfg.num_attention_heads;
   const int rows = max_q_len * H;
   if (L->elem == 2) {
-    if (rows > 32) { p->NB = 2; p->RQ = (rows + 63) / 64; }
+    if (rows >= 128) { p->NB = 4; p->RQ = (rows + 127) / 128; }
+    else if (rows > 32) { p->NB = 2; p->RQ = (rows + 63) / 64; }
     else { p->NB = 1; p->RQ = 1; }
   } else {
     p->NB = 1;
     p->RQ = 1;
   }
   if (kv_chunk > 0) {
-    if (kv_chunk % 64) return false;
+    if (kv_chunk % 64 || kv_chunk > 8192) return false;
     p->chunk = kv_chunk;
   } else {
     // One resident workgroup per compute unit (two when the row block is
@@ -117,7 +119,7 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
     p->chunk = (int)c;
   }
   p->S_max = (max_seq_len + p->chunk - 1) / p->chunk;
-  return true;
+  return p->S_max <= 1024;   // split weights of one row are staged on chip
 }
 
 struct DecodeLayout {
@@ -279,8 +281,8 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
                 batch, total_q, max_q_len, max_seq_len, max_pages);
   if ((int64_t)total_q > (int64_t)batch * max_q_len)
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: total_q exceeds batch * max_q_len");
-  if (kv_chunk < 0 || kv_chunk % 64)
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a positive multiple of 64");
+  if (kv_chunk < 0 || kv_chunk % 64 || kv_chunk > 8192)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a multiple of 64 up to 8192");
   mla::SplitPlan p;
   if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p))
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: cannot plan the split");

@@ -59,39 +59,51 @@ __global__ void append_gemm_f32_kernel(const float* __restrict__ x, const float*
   part[o] = acc;
 }
 
+// One thread per (token, element pair): sum the k-split partials in a fixed
+// order, rotate rope pairs, round, store into the token's page slot.
 template <typename T>
-__global__ void append_finish_kernel(const float* __restrict__ part, int ksplits, int T_new,
-                                     const int32_t* __restrict__ cu_new,
-                                     const int32_t* __restrict__ prefix_lens,
-                                     const int32_t* __restrict__ page_table, int max_pages,
-                                     int batch, T* __restrict__ cache, int page_size, int dc,
-                                     int dr, float base) {
+__global__ __launch_bounds__(64) void append_finish_kernel(
+    const float* __restrict__ part, int ksplits, int T_new, const int32_t* __restrict__ cu_new,
+    const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ page_table, int max_pages,
+    int batch, T* __restrict__ cache, int page_size, int dc, int dr, float base) {
+  __shared__ CuStage cu_st;
+  const int32_t* cu = stage_cu(cu_st, cu_new, batch);
   const int t = blockIdx.x;
   const int D = dc + dr;
-  const int b = seq_of_token(cu_new, batch, t);
-  const int pos = prefix_lens[b] + (t - cu_new[b]);
+  const int p = blockIdx.y * 64 + threadIdx.x;
+  if (p >= D / 2) return;
+  const int b = seq_of_token(cu, batch, t);
+  const int pos = prefix_lens[b] + (t - cu[b]);
   const int page = page_table[(int64_t)b * max_pages + pos / page_size];
   T* dst = cache + ((int64_t)page * page_size + pos % page_size) * D;
+  const int n = 2 * p;
   const int64_t stride = (int64_t)T_new * D;
-  for (int p = threadIdx.x; p < D / 2; p += blockDim.x) {
-    const int n = 2 * p;
-    float u0 = 0.f, u1 = 0.f;
-    const float* src = part + (int64_t)t * D + n;
-    for (int ks = 0; ks < ksplits; ++ks) {
-      u0 += src[ks * stride];
-      u1 += src[ks * stride + 1];
-    }
-    if (n >= dc) {
-      float c, s;
-      rope_cos_sin(pos, (n - dc) >> 1, dr, base, &c, &s);
-      float r0 = u0 * c - u1 * s;
-      float r1 = u0 * s + u1 * c;
-      u0 = r0;
-      u1 = r1;
-    }
-    dst[n] = from_f32<T>(u0);
-    dst[n + 1] = from_f32<T>(u1);
+  const float2* src = reinterpret_cast<const float2*>(part + (int64_t)t * D + n);
+  float u0 = 0.f, u1 = 0.f;
+  int ks = 0;
+  for (; ks + 4 <= ksplits; ks += 4) {
+    float2 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float2*>(
+        reinterpret_cast<const float*>(src) + (ks + j) * stride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { u0 += v[j].x; u1 += v[j].y; }
   }
+  for (; ks < ksplits; ++ks) {
+    const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(src) + ks * stride);
+    u0 += v.x;
+    u1 += v.y;
+  }
+  if (n >= dc) {
+    float c, s;
+    rope_cos_sin(pos, (n - dc) >> 1, dr, base, &c, &s);
+    const float r0 = u0 * c - u1 * s;
+    const float r1 = u0 * s + u1 * c;
+    u0 = r0;
+    u1 = r1;
+  }
+  dst[n] = from_f32<T>(u0);
+  dst[n + 1] = from_f32<T>(u1);
 }
 
 }  // namespace
@@ -116,14 +128,15 @@ void launch_append_finish(int elem, const float* part, int ksplits, int T, const
                           const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
                           int batch, void* cache, int page_size, int dc, int dr, float base,
                           hipStream_t st) {
+  dim3 grid(T, ((dc + dr) / 2 + 63) / 64);
   if (elem == 2)
-    append_finish_kernel<bf16><<<T, 256, 0, st>>>(part, ksplits, T, cu_new, prefix_lens,
-                                                  page_table, max_pages, batch, (bf16*)cache,
-                                                  page_size, dc, dr, base);
+    append_finish_kernel<bf16><<<grid, 64, 0, st>>>(part, ksplits, T, cu_new, prefix_lens, page_table,
+                                                    max_pages, batch, (bf16*)cache, page_size, dc, dr,
+                                                    base);
   else
-    append_finish_kernel<float><<<T, 256, 0, st>>>(part, ksplits, T, cu_new, prefix_lens,
-                                                   page_table, max_pages, batch, (float*)cache,
-                                                   page_size, dc, dr, base);
+    append_finish_kernel<float><<<grid, 64, 0, st>>>(part, ksplits, T, cu_new, prefix_lens, page_table,
+                                                     max_pages, batch, (float*)cache, page_size, dc,
+                                                     dr, base);
 }
 
 }  // namespace mla

@@ -11,6 +11,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
@@ -45,6 +46,21 @@ __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int 
     if (cu[mid] <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Token -> sequence lookups for one workgroup: cu[0..batch] is copied to LDS
+// once (one coalesced pass) when it fits, so each lookup is a binary search
+// in LDS rather than a chain of dependent global loads.
+constexpr int kCuStage = 1025;
+struct CuStage {
+  int32_t v[kCuStage];
+};
+__device__ __forceinline__ const int32_t* stage_cu(CuStage& st, const int32_t* __restrict__ cu,
+                                                   int batch) {
+  if (batch + 1 > kCuStage) return cu;
+  for (int i = threadIdx.x; i <= batch; i += blockDim.x) st.v[i] = cu[i];
+  __syncthreads();
+  return st.v;
 }
 
 // ---------------------------------------------------------------- matrix core

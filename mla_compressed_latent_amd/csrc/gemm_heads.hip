@@ -34,20 +34,22 @@ __global__ __launch_bounds__(64) void absorb_bf16_kernel(
   const int lane = threadIdx.x;
   const int m0 = blockIdx.x * 32, jb = blockIdx.y, h = blockIdx.z;
   const int dq = dn + dr, D = dc + dr;
-  if (jb == dc / 32) {
+  if (jb >= dc / 32) {
+    // rope part: each extra column block rotates 64 (token, pair) elements
+    __shared__ CuStage cu_st;
+    const int32_t* cu = stage_cu(cu_st, cu_q, batch);
     const int npair = dr / 2;
-    for (int idx = lane; idx < 32 * npair; idx += 64) {
-      const int t = m0 + idx / npair, p = idx % npair;
-      if (t >= Tq) break;
-      const int pos = query_position(cu_q, seq_lens, batch, t);
-      const bf16* src = q + ((int64_t)t * H + h) * dq + dn + 2 * p;
-      float c, s;
-      rope_cos_sin(pos, p, dr, base, &c, &s);
-      float x0 = to_f32(src[0]), x1 = to_f32(src[1]);
-      bf16* dst = abuf + ((int64_t)t * H + h) * D + dc + 2 * p;
-      dst[0] = from_f32<bf16>(x0 * c - x1 * s);
-      dst[1] = from_f32<bf16>(x0 * s + x1 * c);
-    }
+    const int idx = (jb - dc / 32) * 64 + lane;
+    const int t = m0 + idx / npair, p = idx % npair;
+    if (t >= Tq || idx >= 32 * npair) return;
+    const int pos = query_position(cu, seq_lens, batch, t);
+    const bf16* src = q + ((int64_t)t * H + h) * dq + dn + 2 * p;
+    float c, s;
+    rope_cos_sin(pos, p, dr, base, &c, &s);
+    const float x0 = to_f32(src[0]), x1 = to_f32(src[1]);
+    bf16* dst = abuf + ((int64_t)t * H + h) * D + dc + 2 * p;
+    dst[0] = from_f32<bf16>(x0 * c - x1 * s);
+    dst[1] = from_f32<bf16>(x0 * s + x1 * c);
     return;
   }
   const int j0 = jb * 32;
@@ -150,7 +152,7 @@ void launch_absorb(int elem, const void* q, const void* wuk_p, void* abuf, const
                    const int32_t* seq_lens, int batch, int Tq, int H, int dn, int dr, int dc,
                    float base, hipStream_t st) {
   if (elem == 2) {
-    dim3 grid((Tq + 31) / 32, dc / 32 + 1, H);
+    dim3 grid((Tq + 31) / 32, dc / 32 + (32 * (dr / 2) + 63) / 64, H);
     absorb_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk_p, (bf16*)abuf, cu_q,
                                             seq_lens, batch, Tq, H, dn, dr, dc, base);
   } else {

@@ -12,19 +12,23 @@
 // row (online softmax), and leaves a normalised partial O and its log-sum-exp;
 // the combine kernel merges the splits.
 //
-// bf16 path (d_c = 512, d_rope = 64), per workgroup of 4 waves:
-//   * a 32-token tile of cached rows is copied HBM -> LDS by the LDS-DMA path
-//     (global_load_lds, 16 B per lane), NBUF tiles in flight; rows are XOR
-//     swizzled in 16-byte chunks so both operand reads below are free of bank
-//     conflicts;
-//   * scores: wave w < NB holds the A rows of row block w (32 rows x 576,
-//     in registers for the whole kernel) and runs S^T = tile . A^T on the
-//     32x32x16 bf16 matrix core (36 MFMAs per tile), then the online softmax
-//     in the accumulator layout (one row per lane pair, shuffles across the
-//     pair);
-//   * the probabilities (bf16) go through LDS to all four waves, each of which
-//     accumulates O^T for all rows over its own quarter of d_c (128 columns;
-//     8*NB MFMAs per tile) reading the tile transposed from LDS.
+// bf16 path (d_c = 512, d_rope = 64), one workgroup of 4 waves per (sequence,
+// split, block of NB * 32 rows):
+//   * 32-token tiles of cached rows are copied HBM -> LDS by the LDS-DMA path
+//     (global_load_lds, 16 bytes per lane, every wave copies 8 rows), three
+//     tiles in flight; 16-byte chunks are swizzled per row (swz) so that both
+//     operand reads below are free of bank conflicts;
+//   * score waves (0 .. NB-1) keep their 32 rows of the score operand (32 x
+//     576 bf16) in registers and compute S^T = tile . A^T on the 32x32x16 bf16
+//     matrix core (36 MFMAs per tile), then the online softmax in the
+//     accumulator layout (one row per lane pair), and hand the bf16
+//     probabilities to LDS;
+//   * value waves (2, 3) each accumulate O^T for all rows over half of d_c
+//     (256 columns, 256 accumulator registers at NB = 2), reading the value
+//     operand straight out of the token-major tile with the transposing LDS
+//     load (ds_read_b64_tr_b16);
+//   * the score waves work one tile ahead of the value waves, so the two kinds
+//     of matrix work overlap; one barrier per tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,9 +41,29 @@ constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kD * 2;
 constexpr int kDmaPerWave = kTileBytes / 16 / 64 / 4;   // 9 wave-wide DMAs per wave per tile
 constexpr float kRescaleThreshold = 8.0f;    // log2 units: P may grow to 2^8 before rescale
+constexpr int kMaxChunkTokens = 8192;         // largest split the attention kernel accepts
+constexpr int kMaxChunkPages = kMaxChunkTokens / 64;
 
-// LDS chunk slot of (token t, 16-byte chunk c) inside a tile.
-__device__ __forceinline__ int tile_slot(int t, int c) { return t * kChunks + (c ^ (t & 7)); }
+constexpr int kNBuf = 4;                      // tiles resident in LDS (3 in flight)
+constexpr int kQkRing = 3;                    // score-operand read groups in flight
+constexpr int kPvRing = 6;                    // value-operand reads in flight
+
+// Chunk swizzle: 16-byte chunk c of token t is stored at position
+// c ^ swz(t) of the token's LDS row.  swz permutes t mod 8 (8 consecutive
+// tokens of one chunk hit 8 different bank quads: conflict-free 16-byte
+// score-operand reads) and gives 4 consecutive tokens (4-aligned) distinct
+// values of swz >> 1 (two neighbouring chunks of them hit 8 different bank
+// quads: conflict-free transposing value-operand reads).
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i mod 4) of the 8-byte words addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ v4bf16 ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) v4bf16*)(const __attribute__((address_space(3))) char*)p);
+}
 
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0],
 // expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
@@ -124,18 +148,358 @@ __device__ __forceinline__ void qk_mfma4_last(f32x16& acc, const bf16x8& a0, con
       : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
 }
 
-template <int NB, int NBUF>
+// Value MFMAs, accumulators pinned to AGPRs: one A operand (a transposed
+// tile fragment) against the probability fragments of NB row blocks.  Starts
+// with two wait states (the A operand was just assembled by vector ALU ops).
+template <int NB>
+__device__ __forceinline__ void pv_mfma(f32x16 (&o)[NB], const bf16x8& a, const bf16x8 (&p)[NB]) {
+  if constexpr (NB == 1) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+        : "+a"(o[0])
+        : "v"(a), "v"(p[0]));
+  } else if constexpr (NB == 2) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+        : "+a"(o[0]), "+a"(o[1])
+        : "v"(a), "v"(p[0]), "v"(p[1]));
+  } else {
+    static_assert(NB == 4, "row blocks");
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3"
+        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
+        : "v"(a), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+  }
+}
+
+// 32 wait states after the last value MFMA before the accumulators are read
+// by ordinary instructions; taking them as operands orders the reads after.
+template <int NB, int NDB>
+__device__ __forceinline__ void pv_drain(f32x16 (&o)[NDB][NB]) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    if constexpr (NB == 1) {
+      asm volatile("s_nop 7" : "+a"(o[db][0]));
+    } else if constexpr (NB == 2) {
+      asm volatile("s_nop 7" : "+a"(o[db][0]), "+a"(o[db][1]));
+    } else {
+      asm volatile("s_nop 7" : "+a"(o[db][0]), "+a"(o[db][1]), "+a"(o[db][2]), "+a"(o[db][3]));
+    }
+  }
+}
+
+template <int NB>
 __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
     float* __restrict__ opart, float* __restrict__ lse) {
-  static_assert(NBUF >= 2 && NBUF <= 5, "tile buffers");
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[NBUF][kTileTok * kD];
+  static_assert(NB == 1 || NB == 2, "row blocks per workgroup");
+  constexpr int kDbPerPv = kDC / 32 / 2;       // 32-wide value blocks per value wave (8)
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[kNBuf][kTileTok * kD];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NB][2][64];
+  __shared__ float alpha_s[2][NB][32];
+  __shared__ float lrow_s[NB][32];
+  __shared__ int pages_s[kMaxChunkPages];
+
+  const int nblocks = batch * S_max * RQ;
+  const int logical = xcd_logical_block(blockIdx.x, nblocks);
+  const int rq = logical % RQ;
+  const int s = (logical / RQ) % S_max;
+  const int b = logical / (RQ * S_max);
+
+  const int q0 = cu_q[b];
+  const int Lq = cu_q[b + 1] - q0;
+  const int L = seq_lens[b];
+  const int R = Lq * H;
+  const int row_base = rq * NB * 32;
+  const int tok_begin = s * chunk;
+  if (row_base >= R || tok_begin >= L) return;
+  const int tok_end = min(tok_begin + chunk, L);
+  const int ntiles = (tok_end - tok_begin + kTileTok - 1) / kTileTok;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5, l32 = lane & 31;
+  const bool score_wave = wave < NB;
+  const bool value_wave = wave >= 2;
+  const int pw = wave - 2;                       // value wave index: dims [256 pw, 256 pw + 256)
+  const int64_t rows_total = (int64_t)Tq * H;
+
+  // ---- page ids of this chunk, staged once
+  const int page0 = tok_begin / page_size;
+  const int npages = (tok_end - 1) / page_size - page0 + 1;
+  for (int i = threadIdx.x; i < npages; i += blockDim.x)
+    pages_s[i] = page_table[(int64_t)b * max_pages + page0 + i];
+
+  // ---- per-lane DMA source offsets (loop invariant): LDS slot (t, c') of a
+  // tile receives global chunk (t, c' ^ swz(t)).  Each wave copies 8 token rows.
+  uint32_t dma_off[kDmaPerWave];
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; ++u) {
+    const int slot = (wave * kDmaPerWave + u) * 64 + lane;
+    const int t = slot / kChunks;
+    dma_off[u] = (uint32_t)(t * kChunks + ((slot % kChunks) ^ swz(t))) * 16u;
+  }
+  const uint32_t lds_tiles = lds_address(&tiles[0][0]);
+  __syncthreads();
+  auto issue_tile = [&](int it) {
+    const int tok0 = tok_begin + it * kTileTok;
+    const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
+    const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
+    const uint32_t lds0 =
+        lds_tiles + (uint32_t)((it % kNBuf) * kTileBytes + wave * kDmaPerWave * 1024);
+#pragma unroll
+    for (int u = 0; u < kDmaPerWave; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
+  };
+
+  // ---- score waves: their 32 rows of the score operand, in registers
+  const int my_row = row_base + wave * 32 + l32;
+  const bool row_ok = score_wave && (my_row < R);
+  const int my_i = row_ok ? my_row / H : 0;
+  const int my_h = row_ok ? my_row % H : 0;
+  const int my_limit = row_ok ? (L - Lq + my_i) : -1;   // last visible position
+  bf16x8 qf[kD / 16];
+  if (score_wave) {
+    const bf16* qrow = abuf + ((int64_t)(q0 + my_i) * H + my_h) * kD + 8 * g;
+    const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      u32x4 v = __builtin_bit_cast(u32x4, load_bf16x8(qrow + 16 * ks));
+      v &= keep;
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // score operand: chunk 2ks+g of token l32 sits at qk_base[ks & 3] + 128 (ks >> 2)
+  uint32_t qk_base[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qk_base[j] = (uint32_t)(l32 * kChunks + ((2 * j + g) ^ swz(l32))) * 16u;
+
+  // value operand through the transposing LDS read: in each 16-lane group,
+  // source lane 4j + q points at 4 dims (4q..4q+3 of the group's 16) of token
+  // 4g + j (+ 8 L + 16 ks); lane 4q' + r receives dim 4q'+r of those 4 tokens.
+  // Address = pv_base[db & 1] + 1152 (16 ks + 8 L) + 128 (db >> 1).
+  uint32_t pv_base[2];
+  {
+    const int k = lane >> 4, sl = lane & 15, j = sl >> 2, q = sl & 3;
+    const int t = 4 * g + j;
+#pragma unroll
+    for (int e1 = 0; e1 < 2; ++e1) {
+      const int c = 32 * (pw & 1) + 4 * e1 + 2 * (k & 1) + (q >> 1);
+      pv_base[e1] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
+    }
+  }
+
+  f32x16 O[kDbPerPv][NB];
+#pragma unroll
+  for (int db = 0; db < kDbPerPv; ++db)
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) O[db][rb] = zero_f32x16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // scores, online softmax and probability fragments of tile `it`.  The tile
+  // fragments stream through a ring of kQkRing groups of 4 (LDS latency is
+  // several MFMA groups long under load), so the matrix core never waits on a
+  // read issued just before it.
+  auto score_tile = [&](int it) {
+    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf][0]);
+    const int tok0 = tok_begin + it * kTileTok;
+    constexpr int kGroups = kD / 64;          // 9 groups of 4 k-steps
+    bf16x8 ring[kQkRing][4];
+#pragma unroll
+    for (int grp = 0; grp < kQkRing; ++grp)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ring[grp][j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * grp);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc;
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) {
+      bf16x8 (&a)[4] = ring[grp % kQkRing];
+      if (grp == 0)
+        qk_mfma4_first(acc, a[0], qf[0], a[1], qf[1], a[2], qf[2], a[3], qf[3]);
+      else if (grp == kGroups - 1)
+        qk_mfma4_last(acc, a[0], qf[4 * grp], a[1], qf[4 * grp + 1], a[2], qf[4 * grp + 2], a[3],
+                      qf[4 * grp + 3]);
+      else
+        qk_mfma4(acc, a[0], qf[4 * grp], a[1], qf[4 * grp + 1], a[2], qf[4 * grp + 2], a[3],
+                 qf[4 * grp + 3]);
+      if (grp + kQkRing < kGroups) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * (grp + kQkRing));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = tok0 + acc_row32(r, lane);
+      acc[r] = (tok <= my_limit) ? acc[r] * scale_log2e : -INFINITY;
+      tmax = fmaxf(tmax, acc[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+    float rs = 0.f;
+    bf16x8 pf0, pf1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // probabilities below 2^-126 of the running max flush to zero
+      const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
+      rs += pv;
+      if (r < 8) pf0[r] = from_f32<bf16>(pv);
+      else pf1[r - 8] = from_f32<bf16>(pv);
+    }
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    pbuf[it & 1][wave][0][lane] = pf0;
+    pbuf[it & 1][wave][1][lane] = pf1;
+    if (g == 0) alpha_s[it & 1][wave][l32] = alpha;
+  };
+
+  // O^T[dim][row] += sum_tok tile[tok][dim] P[row][tok] over this value wave's
+  // 256 dims: 16 (k-step, dim block) steps, transposed reads kPvRing steps ahead.
+  auto value_tile = [&](int it) {
+    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf][0]);
+    constexpr int kSteps = 2 * kDbPerPv;
+    auto frag_addr = [&](int step) {
+      const int ks = step / kDbPerPv, db = step % kDbPerPv;
+      return tileb + pv_base[db & 1] + 128 * (db >> 1) + kChunks * 16 * 16 * ks;
+    };
+    v4bf16 ring[kPvRing][2];
+#pragma unroll
+    for (int st = 0; st < kPvRing; ++st) {
+      ring[st][0] = ds_read_tr16(frag_addr(st));
+      ring[st][1] = ds_read_tr16(frag_addr(st) + kChunks * 16 * 8);
+    }
+    bf16x8 pb[2][NB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) pb[ks][rb] = pbuf[it & 1][rb][ks][lane];
+    {  // rare: a row's running max grew past the threshold -> rescale its O
+      float al[NB];
+      bool any = false;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        al[rb] = alpha_s[it & 1][rb][l32];
+        any |= __any(al[rb] != 1.f);
+      }
+      if (any) {
+        pv_drain<NB, kDbPerPv>(O);
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+          for (int db = 0; db < kDbPerPv; ++db) {
+            O[db][rb] *= al[rb];
+            asm volatile("" : "+a"(O[db][rb]));   // back to the accumulator file, block by block
+          }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int ks = st / kDbPerPv, db = st % kDbPerPv;
+      v4bf16 (&f)[2] = ring[st % kPvRing];
+      const bf16x8 a = __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      pv_mfma<NB>(O[db], a, pb[ks]);
+      if (st + kPvRing < kSteps) {
+        f[0] = ds_read_tr16(frag_addr(st + kPvRing));
+        f[1] = ds_read_tr16(frag_addr(st + kPvRing) + kChunks * 16 * 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The sequence's last tile may end before its 32 rows do; the rows past the
+  // end hold whatever the page held.  Zero them before the value waves read
+  // them, so that zero probabilities never meet a NaN.
+  auto zero_tail = [&](int it) {
+    const int nvalid = tok_end - (tok_begin + it * kTileTok);
+    if (nvalid < kTileTok) {
+      u32x4* rows = reinterpret_cast<u32x4*>(&tiles[it % kNBuf][0]) + nvalid * kChunks;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int i = threadIdx.x; i < (kTileTok - nvalid) * kChunks; i += blockDim.x) rows[i] = z;
+      __syncthreads();
+    }
+  };
+
+  // ---- pipeline: score waves run one tile ahead of value waves
+  for (int p = 0; p < kNBuf - 1; ++p)
+    if (p < ntiles) issue_tile(p);
+  wait_tiles_ahead(min(kNBuf - 2, ntiles - 1));
+  __syncthreads();
+  zero_tail(0);
+  if (score_wave) score_tile(0);
+  for (int it = 0; it < ntiles; ++it) {
+    // tile it+1 must have landed: tiles issued after it are min(ntiles-1, it+2) - (it+1)
+    wait_tiles_ahead(min(ntiles - 1, it + kNBuf - 2) - (it + 1));
+    __syncthreads();   // P(it) and tile it+1 visible; tile it-1 fully consumed
+    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
+    if (it + 1 < ntiles) zero_tail(it + 1);
+    if (score_wave && it + 1 < ntiles) score_tile(it + 1);
+    if (value_wave) value_tile(it);
+  }
+  if (value_wave) pv_drain<NB, kDbPerPv>(O);
+
+  // ---- epilogue: row statistics, then normalised partials
+  if (score_wave) {
+    if (g == 0) lrow_s[wave][l32] = l_run;
+    if (g == 0 && my_row < R) {
+      const int64_t rowg = (int64_t)(q0 + my_i) * H + my_h;
+      lse[(int64_t)s * rows_total + rowg] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (!value_wave) return;
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    const int row = row_base + rb * 32 + l32;
+    if (row >= R) continue;
+    const float lr = lrow_s[rb][l32];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    const int64_t rowg = (int64_t)(q0 + row / H) * H + row % H;
+    float* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + pw * 256;
+#pragma unroll
+    for (int db = 0; db < kDbPerPv; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = O[db][rb][4 * q4 + e] * inv;
+        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * q4 + 4 * g) = v;
+      }
+  }
+}
+
+// 128 rows per workgroup (H*q_len >= 128): every wave scores its own 32 rows
+// and accumulates 128 value columns for all four row blocks, so each cached
+// tile crosses the memory fabric once.  Score operand: d_c part in registers
+// (128 VGPRs), rope part in LDS.  Value accumulators: 4 x 4 blocks = all 256
+// AGPRs of the wave.
+__global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
+    const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
+    int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
+    float* __restrict__ opart, float* __restrict__ lse) {
+  constexpr int NB = 4, kNBuf4 = 3;
+  constexpr int kQReg = kDC / 16;                // 32 k-steps of the score operand in registers
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[kNBuf4][kTileTok * kD];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[NB][2][64];
   __shared__ __attribute__((aligned(16))) bf16x8 qrope_s[NB][kDR / 16][64];
   __shared__ float alpha_s[NB][32];
   __shared__ float lrow_s[NB][32];
+  __shared__ int pages_s[kMaxChunkPages];
 
   const int nblocks = batch * S_max * RQ;
   const int logical = xcd_logical_block(blockIdx.x, nblocks);
@@ -158,38 +522,28 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t rows_total = (int64_t)Tq * H;
 
-  // Per-lane source offsets of this wave's DMA slots (loop invariant).  Slot
-  // (t, c') of the LDS tile receives global chunk (t, c' ^ (t & 7)).
+  const int page0 = tok_begin / page_size;
+  const int npages = (tok_end - 1) / page_size - page0 + 1;
+  for (int i = threadIdx.x; i < npages; i += blockDim.x)
+    pages_s[i] = page_table[(int64_t)b * max_pages + page0 + i];
+
   uint32_t dma_off[kDmaPerWave];
 #pragma unroll
   for (int u = 0; u < kDmaPerWave; ++u) {
     const int slot = (wave * kDmaPerWave + u) * 64 + lane;
     const int t = slot / kChunks;
-    const int c = (slot % kChunks) ^ (t & 7);
-    dma_off[u] = (uint32_t)(t * kChunks + c) * 16u;
+    dma_off[u] = (uint32_t)(t * kChunks + ((slot % kChunks) ^ swz(t))) * 16u;
   }
   const uint32_t lds_tiles = lds_address(&tiles[0][0]);
-  auto issue_tile = [&](int it, int buf) {
-    const int tok0 = tok_begin + it * kTileTok;
-    const int page =
-        __builtin_amdgcn_readfirstlane(page_table[(int64_t)b * max_pages + tok0 / page_size]);
-    const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
-    const uint32_t lds0 = lds_tiles + (uint32_t)(buf * kTileBytes + wave * kDmaPerWave * 1024);
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
-  };
 
-  // ---- this wave's score rows (waves < NB): A operand kept in registers
-  const int my_row = row_base + wave * 32 + l32;         // row within the sequence
-  const bool row_ok = (wave < NB) && (my_row < R);
+  // score rows of this wave
+  const int my_row = row_base + wave * 32 + l32;
+  const bool row_ok = my_row < R;
   const int my_i = row_ok ? my_row / H : 0;
   const int my_h = row_ok ? my_row % H : 0;
-  const int my_limit = row_ok ? (L - Lq + my_i) : -1;    // last visible position
-  // Content part (d_c) of the score operand in registers, rope part in LDS.
-  constexpr int kQReg = kDC / 16;          // 32 k-steps in registers
+  const int my_limit = row_ok ? (L - Lq + my_i) : -1;
   bf16x8 qf[kQReg];
   {
-    // rows outside the sequence read row 0 and are zeroed (no branches)
     const bf16* qrow = abuf + ((int64_t)(q0 + my_i) * H + my_h) * kD + 8 * g;
     const uint32_t keep = row_ok ? 0xffffffffu : 0u;
 #pragma unroll
@@ -197,30 +551,35 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
       u32x4 v = __builtin_bit_cast(u32x4, load_bf16x8(qrow + 16 * ks));
       v &= keep;
       if (ks < kQReg) qf[ks] = __builtin_bit_cast(bf16x8, v);
-      else if (wave < NB) qrope_s[wave][ks - kQReg][lane] = __builtin_bit_cast(bf16x8, v);
+      else qrope_s[wave][ks - kQReg][lane] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  __syncthreads();   // pages and rope operand staged
 
-  // LDS byte offsets inside a tile.  The swizzle only touches the low three
-  // bits of the chunk index, so every read below is one of a few per-lane
-  // base offsets plus a compile-time constant.
-  //   score operand, k-step ks: chunk 2ks+g of token l32
-  //     = qk_base[ks & 3] + 128 * (ks >> 2)
-  //   value operand (token tk, dim): tk = 16ks + 8h + (4g + e),  e < 4, h < 2
-  //     = pv_base[db & 1][e] + 9216 * (2ks + h) + 128 * (db >> 1)
+  auto issue_tile = [&](int it) {
+    const int tok0 = tok_begin + it * kTileTok;
+    const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
+    const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
+    const uint32_t lds0 =
+        lds_tiles + (uint32_t)((it % kNBuf4) * kTileBytes + wave * kDmaPerWave * 1024);
+#pragma unroll
+    for (int u = 0; u < kDmaPerWave; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
+  };
+
   uint32_t qk_base[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    qk_base[j] = (uint32_t)(l32 * kChunks + ((2 * j + g) ^ (l32 & 7))) * 16u;
-  uint32_t pv_base[2][4];
+  for (int j = 0; j < 4; ++j) qk_base[j] = (uint32_t)(l32 * kChunks + ((2 * j + g) ^ swz(l32))) * 16u;
+  // value operand (transposing read), this wave's dims [128 wave, 128 wave + 128)
+  uint32_t pv_base[2];
+  {
+    const int k = lane >> 4, sl = lane & 15, j = sl >> 2, q = sl & 3;
+    const int t = 4 * g + j;
 #pragma unroll
-  for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int dim = wave * 128 + d2 * 32 + l32;
-      const int tk = 4 * g + e;
-      pv_base[d2][e] = (uint32_t)(tk * kChunks + ((dim >> 3) ^ tk)) * 16u + (uint32_t)(dim & 7) * 2u;
+    for (int e1 = 0; e1 < 2; ++e1) {
+      const int c = 16 * wave + 4 * e1 + 2 * (k & 1) + (q >> 1);
+      pv_base[e1] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
     }
+  }
 
   f32x16 O[4][NB];
 #pragma unroll
@@ -229,38 +588,59 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     for (int rb = 0; rb < NB; ++rb) O[db][rb] = zero_f32x16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < ntiles) issue_tile(p, p);
+  auto zero_tail = [&](int it) {
+    const int nvalid = tok_end - (tok_begin + it * kTileTok);
+    if (nvalid < kTileTok) {
+      u32x4* rows = reinterpret_cast<u32x4*>(&tiles[it % kNBuf4][0]) + nvalid * kChunks;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int i = threadIdx.x; i < (kTileTok - nvalid) * kChunks; i += blockDim.x) rows[i] = z;
+      __syncthreads();
+    }
+  };
+
+  for (int p = 0; p < kNBuf4 - 1; ++p)
+    if (p < ntiles) issue_tile(p);
 
   for (int it = 0; it < ntiles; ++it) {
-    wait_tiles_ahead(min(NBUF - 2, ntiles - 1 - it));   // this tile's copies have landed
-    __syncthreads();                                     // ... for every wave; prior tile retired
-    if (it + NBUF - 1 < ntiles) issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
-
-    const int buf = it % NBUF;
-    const char* tileb = reinterpret_cast<const char*>(&tiles[buf][0]);
+    wait_tiles_ahead(min(kNBuf4 - 2, ntiles - 1 - it));
+    __syncthreads();                         // tile it landed everywhere; tile it-1 retired
+    if (it + kNBuf4 - 1 < ntiles) issue_tile(it + kNBuf4 - 1);
+    zero_tail(it);
+    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf4][0]);
     const int tok0 = tok_begin + it * kTileTok;
-    const int nvalid = min(kTileTok, tok_end - tok0);
 
-    if (wave < NB) {
-      // S^T[token][row] = sum_k tile[token][k] * A[row][k]   (36 MFMAs)
+    // ---- scores S^T = tile . A^T for this wave's 32 rows
+    {
+      constexpr int kGroups = kD / 64;
+      constexpr int kRing = 2;
+      bf16x8 ring[kRing][4];
+#pragma unroll
+      for (int grp = 0; grp < kRing; ++grp)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ring[grp][j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * grp);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 acc;
 #pragma unroll
-      for (int grp = 0; grp < kD / 64; ++grp) {
-        bf16x8 a[4], qv[4];
+      for (int grp = 0; grp < kGroups; ++grp) {
+        bf16x8 (&a)[4] = ring[grp % kRing];
+        bf16x8 qv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * grp);
+        for (int j = 0; j < 4; ++j)
           qv[j] = (4 * grp + j < kQReg) ? qf[(4 * grp + j) % kQReg] : qrope_s[wave][j][lane];
-        }
         if (grp == 0)
           qk_mfma4_first(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
-        else if (grp == kD / 64 - 1)
+        else if (grp == kGroups - 1)
           qk_mfma4_last(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
         else
           qk_mfma4(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
+        if (grp + kRing < kGroups) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            a[j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * (grp + kRing));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // online softmax, one row per lane pair (lanes l and l ^ 32)
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -270,13 +650,13 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
-      const float alpha = (m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
       float rs = 0.f;
       bf16x8 pf0, pf1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = exp2f(acc[r] - m_ref);
+        const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
         rs += pv;
         if (r < 8) pf0[r] = from_f32<bf16>(pv);
         else pf1[r - 8] = from_f32<bf16>(pv);
@@ -290,58 +670,65 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     }
     __syncthreads();
 
-    // O^T[dim][row] += sum_tok tile[tok][dim] * P[row][tok], this wave's 128 dims
-    // rare: a row's running max grew past the threshold -> rescale its O
+    // ---- values: O^T += tile^T P^T over this wave's 128 dims, all 4 row blocks
+    {
+      {  // rare: a row's running max grew past the threshold -> rescale its O
+        float al[NB];
+        bool any = false;
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      const float al = alpha_s[rb][l32];
-      if (__any(al != 1.f)) {
+        for (int rb = 0; rb < NB; ++rb) {
+          al[rb] = alpha_s[rb][l32];
+          any |= __any(al[rb] != 1.f);
+        }
+        if (any) {
+          pv_drain<NB, 4>(O);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          O[db][rb] *= al;
-          __builtin_amdgcn_sched_barrier(0);
+          for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              O[db][rb] *= al[rb];
+              asm volatile("" : "+a"(O[db][rb]));
+            }
         }
       }
-    }
-    // tokens at or past nvalid are outside the sequence: zero their values
-    const uint32_t lim_lo = (uint32_t)nvalid;
+      constexpr int kSteps = 8, kRing = 4;
+      auto frag_addr = [&](int st) {
+        const int ks = st / 4, db = st % 4;
+        return tileb + pv_base[db & 1] + 128 * (db >> 1) + kChunks * 16 * 16 * ks;
+      };
+      v4bf16 ring[kRing][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int st = 0; st < kRing; ++st) {
+        ring[st][0] = ds_read_tr16(frag_addr(st));
+        ring[st][1] = ds_read_tr16(frag_addr(st) + kChunks * 16 * 8);
+      }
       bf16x8 pb[NB];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < NB; ++rb) pb[rb] = pbuf[rb][ks][lane];
+      for (int st = 0; st < kSteps; ++st) {
+        const int ks = st / 4, db = st % 4;
+        if (db == 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        u32x4 packed;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          // element pair (e, e+1) of the fragment: tokens tk and tk + 1
-          const int h = e2 >> 1, e = 2 * (e2 & 1);
-          const uint32_t off = 9216u * (2 * ks + h) + 128u * (db >> 1);
-          uint32_t lo = *reinterpret_cast<const unsigned short*>(tileb + pv_base[db & 1][e] + off);
-          uint32_t hi = *reinterpret_cast<const unsigned short*>(tileb + pv_base[db & 1][e + 1] + off);
-          if (nvalid < kTileTok) {
-            const uint32_t tk = 16 * ks + 8 * h + 4 * g + e;
-            lo = tk < lim_lo ? lo : 0u;
-            hi = tk + 1 < lim_lo ? hi : 0u;
-          }
-          packed[e2] = lo | (hi << 16);
+          for (int rb = 0; rb < NB; ++rb) pb[rb] = pbuf[rb][ks][lane];
         }
-        const bf16x8 a = __builtin_bit_cast(bf16x8, packed);
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) O[db][rb] = mfma32(a, pb[rb], O[db][rb]);
+        v4bf16 (&f)[2] = ring[st % kRing];
+        const bf16x8 a = __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        pv_mfma<NB>(O[db], a, pb);
+        if (st + kRing < kSteps) {
+          f[0] = ds_read_tr16(frag_addr(st + kRing));
+          f[1] = ds_read_tr16(frag_addr(st + kRing) + kChunks * 16 * 8);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
+  pv_drain<NB, 4>(O);
 
   // ---- epilogue: row statistics, then normalised partials
-  if (wave < NB) {
-    if (g == 0) lrow_s[wave][l32] = l_run;
-    if (g == 0 && my_row < R) {
-      const int64_t rowg = (int64_t)(q0 + my_i) * H + my_h;
-      lse[(int64_t)s * rows_total + rowg] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
-    }
+  if (g == 0) lrow_s[wave][l32] = l_run;
+  if (g == 0 && my_row < R) {
+    const int64_t rowg = (int64_t)(q0 + my_i) * H + my_h;
+    lse[(int64_t)s * rows_total + rowg] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
   }
   __syncthreads();
 #pragma unroll
@@ -444,6 +831,10 @@ __global__ __launch_bounds__(256) void splitkv_f32_kernel(
 }
 
 // ---------------------------------------------------------------- combine
+// One workgroup per (query, head) row: split weights once, then each thread
+// merges four consecutive latent elements across the splits.
+constexpr int kMaxSplits = 1024;
+
 template <typename T>
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ opart,
                                                       const float* __restrict__ lse,
@@ -451,28 +842,40 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ seq_lens,
                                                       int batch, int Tq, int H, int dc, int chunk,
                                                       T* __restrict__ olat) {
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float red[2];
+  __shared__ CuStage cu_st;
+  const int32_t* cu = stage_cu(cu_st, cu_q, batch);
   const int64_t rowg = blockIdx.x;
   const int t = (int)(rowg / H);
-  const int b = seq_of_token(cu_q, batch, t);
+  const int b = seq_of_token(cu, batch, t);
   const int L = seq_lens[b];
-  const int S_b = (L + chunk - 1) / chunk;
+  const int S_b = min((L + chunk - 1) / chunk, kMaxSplits);
   const int64_t rows_total = (int64_t)Tq * H;
-  float M = -INFINITY;
-  for (int s = 0; s < S_b; ++s) M = fmaxf(M, lse[s * rows_total + rowg]);
-  float wsum = 0.f;
-  for (int s = 0; s < S_b; ++s) {
-    const float x = lse[s * rows_total + rowg];
-    wsum += (x == -INFINITY) ? 0.f : exp2f(x - M);
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int j = threadIdx.x; j < dc; j += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < S_b; ++s) {
+  if (threadIdx.x < 64) {
+    float m = -INFINITY;
+    for (int s = threadIdx.x; s < S_b; s += 64) m = fmaxf(m, lse[s * rows_total + rowg]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float sum = 0.f;
+    for (int s = threadIdx.x; s < S_b; s += 64) {
       const float x = lse[s * rows_total + rowg];
-      if (x == -INFINITY) continue;
-      acc = fmaf(exp2f(x - M), opart[(s * rows_total + rowg) * dc + j], acc);
+      const float w = (x == -INFINITY) ? 0.f : exp2f(x - m);
+      w_s[s] = w;
+      sum += w;
     }
-    olat[rowg * dc + j] = from_f32<T>(acc * inv);
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (threadIdx.x == 0) red[0] = sum > 0.f ? 1.f / sum : 0.f;
+  }
+  __syncthreads();
+  const float inv = red[0];
+  for (int j = 4 * threadIdx.x; j < dc; j += 4 * blockDim.x) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S_b; ++s) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(opart + (s * rows_total + rowg) * dc + j);
+      acc += w_s[s] * v;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) olat[rowg * dc + j + e] = from_f32<T>(acc[e] * inv);
   }
 }
 
@@ -487,17 +890,17 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
     const int nblocks = batch * plan.S_max * plan.RQ;
     switch (plan.NB) {
       case 4:
-        splitkv_bf16_kernel<4, 3><<<nblocks, 256, 0, st>>>(
+        splitkv_bf16_rows128_kernel<<<nblocks, 256, 0, st>>>(
             (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
             page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
         break;
       case 2:
-        splitkv_bf16_kernel<2, 3><<<nblocks, 256, 0, st>>>(
+        splitkv_bf16_kernel<2><<<nblocks, 256, 0, st>>>(
             (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
             page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
         break;
       default:
-        splitkv_bf16_kernel<1, 4><<<nblocks, 256, 0, st>>>(
+        splitkv_bf16_kernel<1><<<nblocks, 256, 0, st>>>(
             (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
             page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
         break;
