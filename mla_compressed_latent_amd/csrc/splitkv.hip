@@ -49,12 +49,12 @@ constexpr int kQkRing = 3;                    // score-operand read groups in fl
 constexpr int kPvRing = 6;                    // value-operand reads in flight
 
 // Chunk swizzle: 16-byte chunk c of token t is stored at position
-// c ^ swz(t) of the token's LDS row.  swz permutes t mod 8 (8 consecutive
-// tokens of one chunk hit 8 different bank quads: conflict-free 16-byte
-// score-operand reads) and gives 4 consecutive tokens (4-aligned) distinct
-// values of swz >> 1 (two neighbouring chunks of them hit 8 different bank
-// quads: conflict-free transposing value-operand reads).
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// c ^ swz(t) of the token's LDS row (the XOR stays inside c's aligned group of
+// 8, so the 72 chunks of a row stay in the row).  LDS on gfx950 has 64 banks;
+// swz mixes token bits 1..3 with bit 4 so that the score-operand reads (one
+// chunk of 32 consecutive tokens per half wave) spread over all banks; the
+// transposing value-operand reads stay conflict-light too (measured).
+__device__ __forceinline__ int swz(int t) { return ((t >> 1) ^ (t >> 4)) & 7; }
 
 typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 
@@ -195,6 +195,68 @@ __device__ __forceinline__ void pv_drain(f32x16 (&o)[NDB][NB]) {
   }
 }
 
+// Both halves of a wave hold the same 32 rows (acc_row32: lane l and l ^ 32
+// hold different tokens of row l % 32).  permlane32_swap hands each lane its
+// partner's value without going through LDS; r[0] is the lower half's value
+// and r[1] the upper half's in every lane, so both halves combine them in the
+// same order and agree bit for bit.
+__device__ __forceinline__ float2 lane_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Online softmax over one 32-token tile held in the score accumulator
+// (row l % 32, token tok0 + acc_row32(r, l)).  Scores are scaled into log2
+// units; tokens past the row's last visible position `limit` are masked
+// (only needed when the tile reaches past the smallest limit of the block).
+// The running max moves lazily: only when a score exceeds it by more than
+// kRescaleThreshold, so rescaling O is rare and P stays below 2^threshold.
+// Returns the rescale factor alpha for O; writes the bf16 probabilities as the
+// two k-step fragments of the value MFMA.
+__device__ __forceinline__ float softmax_tile(f32x16& acc, bool masked, int tok0, int limit,
+                                              float scale_log2e, float& m_run, float& l_run,
+                                              bf16x8& pf0, bf16x8& pf1) {
+  const int lane = threadIdx.x & 63;
+  float tmax = -INFINITY;
+  if (masked) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = tok0 + acc_row32(r, lane);
+      acc[r] = (tok <= limit) ? acc[r] * scale_log2e : -INFINITY;
+      tmax = fmaxf(tmax, acc[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[r] *= scale_log2e;
+      tmax = fmaxf(tmax, acc[r]);
+    }
+  }
+  {
+    const float2 h = lane_halves(tmax);
+    tmax = fmaxf(h.x, h.y);
+  }
+  const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
+  const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+  const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    // probabilities below 2^-126 of the running max flush to zero
+    const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
+    rs += pv;
+    if (r < 8) pf0[r] = from_f32<bf16>(pv);
+    else pf1[r - 8] = from_f32<bf16>(pv);
+  }
+  {
+    const float2 h = lane_halves(rs);
+    rs = h.x + h.y;
+  }
+  l_run = l_run * alpha + rs;
+  m_run = m_new;
+  return alpha;
+}
+
 template <int NB>
 __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
@@ -284,17 +346,21 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
 
   // value operand through the transposing LDS read: in each 16-lane group,
   // source lane 4j + q points at 4 dims (4q..4q+3 of the group's 16) of token
-  // 4g + j (+ 8 L + 16 ks); lane 4q' + r receives dim 4q'+r of those 4 tokens.
-  // Address = pv_base[db & 1] + 1152 (16 ks + 8 L) + 128 (db >> 1).
-  uint32_t pv_base[2];
+  // 4g + j + 8 L + 16 ks; lane 4q' + r receives dim 4q'+r of those 4 tokens.
+  // The swizzle depends on the token: +16 tokens flips chunk bit 0 (a base of
+  // its own), +8 tokens flips chunk bit 2, i.e. swaps the two e1 bases.
+  // Address = pv_base[(db & 1) ^ L][ks] + 9216 L + 128 (db >> 1).
+  uint32_t pv_base[2][2];
   {
     const int k = lane >> 4, sl = lane & 15, j = sl >> 2, q = sl & 3;
-    const int t = 4 * g + j;
 #pragma unroll
-    for (int e1 = 0; e1 < 2; ++e1) {
-      const int c = 32 * (pw & 1) + 4 * e1 + 2 * (k & 1) + (q >> 1);
-      pv_base[e1] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
-    }
+    for (int e1 = 0; e1 < 2; ++e1)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int t = 4 * g + j + 16 * ks;
+        const int c = 32 * (pw & 1) + 4 * e1 + 2 * (k & 1) + (q >> 1);
+        pv_base[e1][ks] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
+      }
   }
 
   f32x16 O[kDbPerPv][NB];
@@ -338,30 +404,9 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = tok0 + acc_row32(r, lane);
-      acc[r] = (tok <= my_limit) ? acc[r] * scale_log2e : -INFINITY;
-      tmax = fmaxf(tmax, acc[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
-    const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    float rs = 0.f;
     bf16x8 pf0, pf1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // probabilities below 2^-126 of the running max flush to zero
-      const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
-      rs += pv;
-      if (r < 8) pf0[r] = from_f32<bf16>(pv);
-      else pf1[r - 8] = from_f32<bf16>(pv);
-    }
-    rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+    const bool masked = tok0 + kTileTok - 1 > L - Lq;
+    const float alpha = softmax_tile(acc, masked, tok0, my_limit, scale_log2e, m_run, l_run, pf0, pf1);
     pbuf[it & 1][wave][0][lane] = pf0;
     pbuf[it & 1][wave][1][lane] = pf1;
     if (g == 0) alpha_s[it & 1][wave][l32] = alpha;
@@ -372,15 +417,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   auto value_tile = [&](int it) {
     const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf][0]);
     constexpr int kSteps = 2 * kDbPerPv;
-    auto frag_addr = [&](int step) {
+    auto frag_addr = [&](int step, int hl) {
       const int ks = step / kDbPerPv, db = step % kDbPerPv;
-      return tileb + pv_base[db & 1] + 128 * (db >> 1) + kChunks * 16 * 16 * ks;
+      return tileb + pv_base[(db & 1) ^ hl][ks] + kChunks * 16 * 8 * hl + 128 * (db >> 1);
     };
     v4bf16 ring[kPvRing][2];
 #pragma unroll
     for (int st = 0; st < kPvRing; ++st) {
-      ring[st][0] = ds_read_tr16(frag_addr(st));
-      ring[st][1] = ds_read_tr16(frag_addr(st) + kChunks * 16 * 8);
+      ring[st][0] = ds_read_tr16(frag_addr(st, 0));
+      ring[st][1] = ds_read_tr16(frag_addr(st, 1));
     }
     bf16x8 pb[2][NB];
 #pragma unroll
@@ -414,8 +459,8 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
       const bf16x8 a = __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7);
       pv_mfma<NB>(O[db], a, pb[ks]);
       if (st + kPvRing < kSteps) {
-        f[0] = ds_read_tr16(frag_addr(st + kPvRing));
-        f[1] = ds_read_tr16(frag_addr(st + kPvRing) + kChunks * 16 * 8);
+        f[0] = ds_read_tr16(frag_addr(st + kPvRing, 0));
+        f[1] = ds_read_tr16(frag_addr(st + kPvRing, 1));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -570,15 +615,17 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) qk_base[j] = (uint32_t)(l32 * kChunks + ((2 * j + g) ^ swz(l32))) * 16u;
   // value operand (transposing read), this wave's dims [128 wave, 128 wave + 128)
-  uint32_t pv_base[2];
+  uint32_t pv_base[2][2];
   {
     const int k = lane >> 4, sl = lane & 15, j = sl >> 2, q = sl & 3;
-    const int t = 4 * g + j;
 #pragma unroll
-    for (int e1 = 0; e1 < 2; ++e1) {
-      const int c = 16 * wave + 4 * e1 + 2 * (k & 1) + (q >> 1);
-      pv_base[e1] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
-    }
+    for (int e1 = 0; e1 < 2; ++e1)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int t = 4 * g + j + 16 * ks;
+        const int c = 16 * wave + 4 * e1 + 2 * (k & 1) + (q >> 1);
+        pv_base[e1][ks] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
+      }
   }
 
   f32x16 O[4][NB];
@@ -641,29 +688,9 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tok0 + acc_row32(r, lane);
-        acc[r] = (tok <= my_limit) ? acc[r] * scale_log2e : -INFINITY;
-        tmax = fmaxf(tmax, acc[r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
-      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      float rs = 0.f;
       bf16x8 pf0, pf1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
-        rs += pv;
-        if (r < 8) pf0[r] = from_f32<bf16>(pv);
-        else pf1[r - 8] = from_f32<bf16>(pv);
-      }
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      const bool masked = tok0 + kTileTok - 1 > L - Lq;
+      const float alpha = softmax_tile(acc, masked, tok0, my_limit, scale_log2e, m_run, l_run, pf0, pf1);
       pbuf[wave][0][lane] = pf0;
       pbuf[wave][1][lane] = pf1;
       if (g == 0) alpha_s[wave][l32] = alpha;
@@ -692,15 +719,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
         }
       }
       constexpr int kSteps = 8, kRing = 4;
-      auto frag_addr = [&](int st) {
+      auto frag_addr = [&](int st, int hl) {
         const int ks = st / 4, db = st % 4;
-        return tileb + pv_base[db & 1] + 128 * (db >> 1) + kChunks * 16 * 16 * ks;
+        return tileb + pv_base[(db & 1) ^ hl][ks] + kChunks * 16 * 8 * hl + 128 * (db >> 1);
       };
       v4bf16 ring[kRing][2];
 #pragma unroll
       for (int st = 0; st < kRing; ++st) {
-        ring[st][0] = ds_read_tr16(frag_addr(st));
-        ring[st][1] = ds_read_tr16(frag_addr(st) + kChunks * 16 * 8);
+        ring[st][0] = ds_read_tr16(frag_addr(st, 0));
+        ring[st][1] = ds_read_tr16(frag_addr(st, 1));
       }
       bf16x8 pb[NB];
       __builtin_amdgcn_sched_barrier(0);
@@ -715,8 +742,8 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
         const bf16x8 a = __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7);
         pv_mfma<NB>(O[db], a, pb);
         if (st + kRing < kSteps) {
-          f[0] = ds_read_tr16(frag_addr(st + kRing));
-          f[1] = ds_read_tr16(frag_addr(st + kRing) + kChunks * 16 * 8);
+          f[0] = ds_read_tr16(frag_addr(st + kRing, 0));
+          f[1] = ds_read_tr16(frag_addr(st + kRing, 1));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
