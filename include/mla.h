@@ -69,8 +69,8 @@ typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
 
 /* Shape of one MLA layer.  Field names follow the Hugging Face DeepSeek-V2
  * config.  bf16 layers need kv_lora_rank == 512, qk_rope_head_dim == 64,
- * qk_nope_head_dim and v_head_dim multiples of 32 and d_model a multiple of
- * 256 (the matrix-core path); fp32 layers accept positive sizes with an
+ * qk_nope_head_dim (at most 256) and v_head_dim multiples of 32 and d_model a
+ * multiple of 256 (the matrix-core path); fp32 layers accept positive sizes with an
  * even qk_rope_head_dim and a kv_lora_rank that is a multiple of 4, at most
  * 1024. */
 typedef struct {

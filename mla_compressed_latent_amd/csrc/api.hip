@@ -15,9 +15,11 @@ struct mla_layer {
   mla_config cfg;
   int elem;        // bytes per stored element
   float scale;     // softmax scale actually used
-  void* wdkv_t;    // [D][d_model]
-  void* wuk_p;     // [H][d_c][d_nope]
-  void* wuv_p;     // [H][d_v][d_c]
+  // folded weights: fragment-tiled for bf16, transposed row-major for fp32
+  void* wdkv_t;    // rows n < D, k = d < d_model
+  void* wuk_p;     // per head: rows j < d_c, k = i < d_nope
+  void* wuv_p;     // per head: rows v < d_v, k = j < d_c
+  mla::RopeFreq freq;   // rotary frequencies (bf16 layers)
   int num_cus;
 };
 
@@ -53,8 +55,9 @@ mla_status check_config(const mla_config* c) {
   if (c->dtype == MLA_DTYPE_BF16) {
     if (c->kv_lora_rank != 512 || c->qk_rope_head_dim != 64)
       return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need kv_lora_rank 512 and qk_rope_head_dim 64");
-    if (c->qk_nope_head_dim % 32 || c->v_head_dim % 32)
-      return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need qk_nope_head_dim, v_head_dim multiples of 32");
+    if (c->qk_nope_head_dim % 32 || c->v_head_dim % 32 || c->qk_nope_head_dim > 256)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "bf16 layers need qk_nope_head_dim (<= 256) and v_head_dim multiples of 32");
     if (c->d_model % 256)
       return fail(MLA_ERR_UNSUPPORTED, "bf16 layers need d_model to be a multiple of 256");
   } else if (c->dtype == MLA_DTYPE_F32) {
@@ -193,6 +196,8 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
   L->wuk_p = (char*)folded + f.off_wuk;
   L->wuv_p = (char*)folded + f.off_wuv;
   L->num_cus = ncu;
+  for (int i = 0; i < mla::kRopePairs; ++i)
+    L->freq.theta[i] = pow((double)cfg->rope_base, -2.0 * i / (double)cfg->qk_rope_head_dim);
   mla::launch_pack(L->elem, w_dkv, w_uk, w_uv, L->wdkv_t, L->wuk_p, L->wuv_p, cfg->d_model,
                    cfg->num_attention_heads, cfg->qk_nope_head_dim, cfg->v_head_dim,
                    cfg->kv_lora_rank, cfg->qk_rope_head_dim, (hipStream_t)hip_stream);
@@ -242,7 +247,7 @@ mla_status mla_append_latent(const mla_layer* L, const void* x, const int32_t* c
   }
   mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
                             batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
-                            st);
+                            L->freq, st);
   return hip_check("append launch");
 }
 
@@ -300,14 +305,22 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
   void* olat = ws + d.off_olat;
   const int H = c.num_attention_heads;
   if (phases & MLA_PHASE_ABSORB)
-    mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, H, c.qk_nope_head_dim,
-                       c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, st);
+    mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, max_q_len, H,
+                       c.qk_nope_head_dim, c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, L->freq,
+                       st);
   if (phases & MLA_PHASE_ATTEND)
     mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse, st);
   if (phases & MLA_PHASE_OUTPUT) {
-    mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank, olat, st);
-    mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim, st);
+    if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
+      mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
+                              c.v_head_dim, st);
+    } else {
+      mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank,
+                          olat, st);
+      mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim,
+                           st);
+    }
   }
   return hip_check("decode launch");
 }

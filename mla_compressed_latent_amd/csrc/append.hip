@@ -18,31 +18,34 @@ namespace {
 
 constexpr int kAppendKChunk = 256;   // d_model elements per split
 
-// One wave computes a 32 (tokens) x 32 (row elements) tile over one k chunk.
+// One wave: u^T block (32 row elements x 32 tokens) over one k chunk, the
+// folded W_dkv as the A operand (contiguous fragments), the hidden states as
+// the B operand.  Each lane stores 4 consecutive row elements of one token.
 __global__ __launch_bounds__(64) void append_gemm_bf16_kernel(const bf16* __restrict__ x,
-                                                              const bf16* __restrict__ wt,
+                                                              const bf16* __restrict__ wdkv,
                                                               float* __restrict__ part, int M,
                                                               int N, int K) {
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32, ks = blockIdx.z;
-  const int k0 = ks * kAppendKChunk + 8 * (lane >> 5);
-  const int mrow = min(m0 + (lane & 31), M - 1);
-  const bf16* xa = x + (int64_t)mrow * K + k0;
-  const bf16* wb = wt + (int64_t)(n0 + (lane & 31)) * K + k0;
-  bf16x8 a[kAppendKChunk / 16], b[kAppendKChunk / 16];
+  constexpr int NS = kAppendKChunk / 16;
+  const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.x * 32, nb = blockIdx.y, ks = blockIdx.z;
+  const int t = m0 + l32;
+  const bf16* xr = x + (int64_t)min(t, M - 1) * K + ks * kAppendKChunk + 8 * g;
+  bf16x8 a[NS], b[NS];
 #pragma unroll
-  for (int s = 0; s < kAppendKChunk / 16; ++s) {
-    a[s] = load_bf16x8(xa + 16 * s);
-    b[s] = load_bf16x8(wb + 16 * s);
+  for (int s = 0; s < NS; ++s) {
+    a[s] = load_fragment(wdkv, nb, ks * NS + s, K, lane);
+    b[s] = load_bf16x8(xr + 16 * s);
   }
   f32x16 acc = zero_f32x16();
 #pragma unroll
-  for (int s = 0; s < kAppendKChunk / 16; ++s) acc = mfma32(a[s], b[s], acc);
-  float* out = part + (int64_t)ks * M * N;
+  for (int s = 0; s < NS; ++s) acc = mfma32(a[s], b[s], acc);
+  if (t < M) {
+    float* out = part + ((int64_t)ks * M + t) * N + nb * 32 + 4 * g;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    int m = m0 + acc_row32(r, lane);
-    if (m < M) out[(int64_t)m * N + n0 + (lane & 31)] = acc[r];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+      *reinterpret_cast<f32x4*>(out + 8 * r4) = v;
+    }
   }
 }
 
@@ -65,7 +68,8 @@ template <typename T>
 __global__ __launch_bounds__(64) void append_finish_kernel(
     const float* __restrict__ part, int ksplits, int T_new, const int32_t* __restrict__ cu_new,
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ page_table, int max_pages,
-    int batch, T* __restrict__ cache, int page_size, int dc, int dr, float base) {
+    int batch, T* __restrict__ cache, int page_size, int dc, int dr, float base,
+    const RopeFreq freq) {
   __shared__ CuStage cu_st;
   const int32_t* cu = stage_cu(cu_st, cu_new, batch);
   const int t = blockIdx.x;
@@ -96,7 +100,10 @@ __global__ __launch_bounds__(64) void append_finish_kernel(
   }
   if (n >= dc) {
     float c, s;
-    rope_cos_sin(pos, (n - dc) >> 1, dr, base, &c, &s);
+    if constexpr (sizeof(T) == 2)
+      rope_cos_sin_reduced(pos, freq.theta[(n - dc) >> 1], &c, &s);   // bf16: d_rope = 64
+    else
+      rope_cos_sin(pos, (n - dc) >> 1, dr, base, &c, &s);
     const float r0 = u0 * c - u1 * s;
     const float r1 = u0 * s + u1 * c;
     u0 = r0;
@@ -110,10 +117,10 @@ __global__ __launch_bounds__(64) void append_finish_kernel(
 
 int append_ksplits_bf16(int K) { return K / kAppendKChunk; }
 
-void launch_append_gemm_bf16(const void* x, const void* wt, float* part, int M, int N, int K,
+void launch_append_gemm_bf16(const void* x, const void* wdkv, float* part, int M, int N, int K,
                              hipStream_t st) {
   dim3 grid((M + 31) / 32, N / 32, K / kAppendKChunk);
-  append_gemm_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)x, (const bf16*)wt, part, M, N, K);
+  append_gemm_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)x, (const bf16*)wdkv, part, M, N, K);
 }
 
 void launch_append_gemm_f32(const void* x, const void* wt, float* part, int M, int N, int K,
@@ -127,16 +134,16 @@ void launch_append_gemm_f32(const void* x, const void* wt, float* part, int M, i
 void launch_append_finish(int elem, const float* part, int ksplits, int T, const int32_t* cu_new,
                           const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
                           int batch, void* cache, int page_size, int dc, int dr, float base,
-                          hipStream_t st) {
+                          const RopeFreq& freq, hipStream_t st) {
   dim3 grid(T, ((dc + dr) / 2 + 63) / 64);
   if (elem == 2)
     append_finish_kernel<bf16><<<grid, 64, 0, st>>>(part, ksplits, T, cu_new, prefix_lens, page_table,
                                                     max_pages, batch, (bf16*)cache, page_size, dc, dr,
-                                                    base);
+                                                    base, freq);
   else
     append_finish_kernel<float><<<grid, 64, 0, st>>>(part, ksplits, T, cu_new, prefix_lens, page_table,
                                                      max_pages, batch, (float*)cache, page_size, dc,
-                                                     dr, base);
+                                                     dr, base, freq);
 }
 
 }  // namespace mla

@@ -37,6 +37,25 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int pair, int d_rope, floa
   *s = static_cast<float>(sd);
 }
 
+// Rotary frequencies of a bf16 layer (d_rope = 64), computed once on the
+// host in double: theta_i = base^(-2i/d_rope).
+constexpr int kRopePairs = 32;
+struct RopeFreq {
+  double theta[kRopePairs];
+};
+
+// cos/sin of pos * theta: the angle is formed and reduced modulo 2 pi in
+// double (2 pi split into two doubles), and only the reduced angle in
+// [-pi, pi] goes through single-precision sincos -- accurate to a few 1e-7
+// at positions past 1e5, far below the bf16 rounding of the rotated values.
+__device__ __forceinline__ void rope_cos_sin_reduced(int pos, double theta, float* c, float* s) {
+  const double a = (double)pos * theta;
+  const double k = rint(a * 0.15915494309189535);
+  double r = fma(-k, 6.283185307179586, a);
+  r = fma(-k, 2.4492935982947064e-16, r);
+  sincosf((float)r, s, c);
+}
+
 // Index of the sequence that owns flat token t, given cu[0..batch] (cu[0]=0,
 // nondecreasing).  Largest b with cu[b] <= t.
 __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int batch, int t) {
@@ -90,6 +109,21 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
+}
+
+// Fragment-tiled operand layout of a bf16 matrix with R rows (R % 32 == 0)
+// and contraction length K (K % 16 == 0), used for the folded weights: the
+// fragment of row block rb and k-step s is 64 lanes x 8 elements, lane l
+// holding row 32 rb + l % 32 and k = 16 s + 8 (l / 32) + 0..7 -- exactly
+// one operand of the 32x32x16 matrix instruction -- so a wave fetches it with
+// one contiguous 1 KB read.
+__host__ __device__ __forceinline__ int64_t tiled_index(int row, int k, int K) {
+  return (((int64_t)(row >> 5) * (K >> 4) + (k >> 4)) * 64 + (row & 31) + 32 * ((k >> 3) & 1)) * 8 +
+         (k & 7);
+}
+__device__ __forceinline__ bf16x8 load_fragment(const bf16* __restrict__ base, int rb, int s, int K,
+                                                int lane) {
+  return load_bf16x8(base + (((int64_t)rb * (K >> 4) + s) * 64 + lane) * 8);
 }
 
 // XCD-aware block order: the hardware deals consecutive workgroup ids to the

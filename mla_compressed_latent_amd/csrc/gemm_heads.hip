@@ -25,80 +25,269 @@ __device__ __forceinline__ int query_position(const int32_t* __restrict__ cu_q,
   return seq_lens[b] - (cu_q[b + 1] - cu_q[b]) + (t - cu_q[b]);
 }
 
-// One wave: 32 tokens x 32 latent columns of one head, or (last column block)
-// the rotated rope part of 32 tokens of that head.
+constexpr int kAbsorbJB = 2;      // 32-column blocks of q_lat per wave
+constexpr int kRopeTok = 4;       // query tokens per rope workgroup
+constexpr int kRopeHeads = 16;    // heads per rope workgroup
+
+__device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {from_f32<bf16>(a), from_f32<bf16>(b), from_f32<bf16>(c), from_f32<bf16>(d)};
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+
+// q_lat^T block = W_uk_h^T (32 latent rows x d_nope) . q_nope^T (d_nope x 32
+// tokens): the folded weight is the A operand, streamed as contiguous
+// fragments; the 32 query rows are the B operand.  One wave per (32-token
+// block, head, kAbsorbJB column blocks); each lane stores 4 consecutive
+// latent values of one token.
+//
+// Workgroups past the GEMM blocks rotate the rope part of the queries: one
+// per (sequence, block of kRopeTok of its query tokens, block of kRopeHeads
+// heads), so each angle is computed once and applied to every head of the
+// block.  Lane l handles pair l % 32 (d_rope = 64) for heads of parity l / 32.
+template <int NS>   // d_nope / 16
 __global__ __launch_bounds__(64) void absorb_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ wuk_p, bf16* __restrict__ abuf,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int batch, int Tq,
-    int H, int dn, int dr, int dc, float base) {
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * 32, jb = blockIdx.y, h = blockIdx.z;
-  const int dq = dn + dr, D = dc + dr;
-  if (jb >= dc / 32) {
-    // rope part: each extra column block rotates 64 (token, pair) elements
-    __shared__ CuStage cu_st;
-    const int32_t* cu = stage_cu(cu_st, cu_q, batch);
-    const int npair = dr / 2;
-    const int idx = (jb - dc / 32) * 64 + lane;
-    const int t = m0 + idx / npair, p = idx % npair;
-    if (t >= Tq || idx >= 32 * npair) return;
-    const int pos = query_position(cu, seq_lens, batch, t);
-    const bf16* src = q + ((int64_t)t * H + h) * dq + dn + 2 * p;
-    float c, s;
-    rope_cos_sin(pos, p, dr, base, &c, &s);
-    const float x0 = to_f32(src[0]), x1 = to_f32(src[1]);
-    bf16* dst = abuf + ((int64_t)t * H + h) * D + dc + 2 * p;
-    dst[0] = from_f32<bf16>(x0 * c - x1 * s);
-    dst[1] = from_f32<bf16>(x0 * s + x1 * c);
+    const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
+    int dc, int gemm_blocks, int TC, const RopeFreq freq) {
+  constexpr int dn = NS * 16;
+  const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
+  if ((int)blockIdx.x >= gemm_blocks) {
+    const int p = l32, hpar = g;
+    const int HG = (H + kRopeHeads - 1) / kRopeHeads;
+    const int rid = blockIdx.x - gemm_blocks;
+    const int hg = rid % HG, tc = (rid / HG) % TC, b = rid / (HG * TC);
+    const int q0 = cu_q[b], Lq = cu_q[b + 1] - q0, L = seq_lens[b];
+    const int dq = dn + dr, D = dc + dr;
+    const double theta = freq.theta[p];
+    for (int i = tc * kRopeTok; i < min(Lq, (tc + 1) * kRopeTok); ++i) {
+      const int64_t t = q0 + i;
+      uint32_t v[kRopeHeads / 2];
+#pragma unroll
+      for (int m = 0; m < kRopeHeads / 2; ++m) {
+        const int h = hg * kRopeHeads + hpar + 2 * m;
+        if (h < H) v[m] = *reinterpret_cast<const uint32_t*>(q + (t * H + h) * dq + dn + 2 * p);
+      }
+      float c, sn;
+      rope_cos_sin_reduced(L - Lq + i, theta, &c, &sn);
+#pragma unroll
+      for (int m = 0; m < kRopeHeads / 2; ++m) {
+        const int h = hg * kRopeHeads + hpar + 2 * m;
+        if (h >= H) continue;
+        const float x0 = __uint_as_float(v[m] << 16), x1 = __uint_as_float(v[m] & 0xffff0000u);
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 r = {from_f32<bf16>(x0 * c - x1 * sn), from_f32<bf16>(x0 * sn + x1 * c)};
+        *reinterpret_cast<bf16x2*>(abuf + (t * H + h) * D + dc + 2 * p) = r;
+      }
+    }
     return;
   }
-  const int j0 = jb * 32;
-  const int trow = min(m0 + (lane & 31), Tq - 1);
-  const bf16* qa = q + ((int64_t)trow * H + h) * dq + 8 * (lane >> 5);
-  const bf16* wb = wuk_p + ((int64_t)h * dc + j0 + (lane & 31)) * dn + 8 * (lane >> 5);
-  f32x16 acc = zero_f32x16();
-  for (int k = 0; k < dn; k += 64) {
-    bf16x8 a[4], b[4];
+  const int JG = dc / 32 / kAbsorbJB;
+  const int id = blockIdx.x;
+  const int jg = id % JG, h = (id / JG) % H, tb = id / (JG * H);
+  const int dq = dn + dr, D = dc + dr;
+  const int t = tb * 32 + l32;
+  const bf16* qrow = q + ((int64_t)min(t, Tq - 1) * H + h) * dq + 8 * g;
+  const bf16* wh = wuk + (int64_t)h * dc * dn;
+  bf16x8 bq[NS], wa[kAbsorbJB][NS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bool in = k + 16 * s < dn;
-      a[s] = in ? load_bf16x8(qa + k + 16 * s) : zero_bf16x8();
-      b[s] = in ? load_bf16x8(wb + k + 16 * s) : zero_bf16x8();
+  for (int jb = 0; jb < kAbsorbJB; ++jb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wa[jb][s] = load_fragment(wh, jg * kAbsorbJB + jb, s, dn, lane);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) bq[s] = load_bf16x8(qrow + 16 * s);
+#pragma unroll
+  for (int jb = 0; jb < kAbsorbJB; ++jb) {
+    f32x16 acc = zero_f32x16();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32(wa[jb][s], bq[s], acc);
+    if (t < Tq) {
+      bf16* dst = abuf + ((int64_t)t * H + h) * D + (jg * kAbsorbJB + jb) * 32 + 4 * g;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store_bf16x4(dst + 8 * r4, acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma32(a[s], b[s], acc);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = m0 + acc_row32(r, lane);
-    if (t < Tq) abuf[((int64_t)t * H + h) * D + j0 + (lane & 31)] = from_f32<bf16>(acc[r]);
   }
 }
 
+// out^T block = W_uv_h^T (32 value rows x d_c) . o_lat^T (d_c x 32 tokens).
+// One wave per (32-token block, head, 32 value columns); the 32 k-steps of
+// both operands stream in groups of 8, two groups in flight.
 __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restrict__ olat,
-                                                           const bf16* __restrict__ wuv_p,
+                                                           const bf16* __restrict__ wuv,
                                                            bf16* __restrict__ out, int Tq, int H,
-                                                           int dc, int dv) {
-  const int lane = threadIdx.x;
-  const int m0 = blockIdx.x * 32, v0 = blockIdx.y * 32, h = blockIdx.z;
-  const int trow = min(m0 + (lane & 31), Tq - 1);
-  const bf16* oa = olat + ((int64_t)trow * H + h) * dc + 8 * (lane >> 5);
-  const bf16* wb = wuv_p + ((int64_t)h * dv + v0 + (lane & 31)) * dc + 8 * (lane >> 5);
-  f32x16 acc = zero_f32x16();
-  for (int k = 0; k < dc; k += 128) {
-    bf16x8 a[8], b[8];
+                                                           int dv) {
+  constexpr int kDc = 512, NS = kDc / 16, kGrp = 8, NG = NS / kGrp;
+  const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
+  const int VB = dv / 32;
+  const int id = blockIdx.x;
+  const int vb = id % VB, h = (id / VB) % H, tb = id / (VB * H);
+  const int t = tb * 32 + l32;
+  const bf16* orow = olat + ((int64_t)min(t, Tq - 1) * H + h) * kDc + 8 * g;
+  const bf16* wh = wuv + (int64_t)h * dv * kDc;
+  bf16x8 a[2][kGrp], b[2][kGrp];
+  auto load_group = [&](int grp, int slot) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      a[s] = load_bf16x8(oa + k + 16 * s);
-      b[s] = load_bf16x8(wb + k + 16 * s);
+    for (int u = 0; u < kGrp; ++u) {
+      a[slot][u] = load_fragment(wh, vb, grp * kGrp + u, kDc, lane);
+      b[slot][u] = load_bf16x8(orow + 16 * (grp * kGrp + u));
+    }
+  };
+  load_group(0, 0);
+  load_group(1, 1);
+  f32x16 acc = zero_f32x16();
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) acc = mfma32(a[grp & 1][u], b[grp & 1][u], acc);
+    if (grp + 2 < NG) load_group(grp + 2, grp & 1);
+  }
+  if (t < Tq) {
+    bf16* dst = out + ((int64_t)t * H + h) * dv + vb * 32 + 4 * g;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      store_bf16x4(dst + 8 * r4, acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]);
+  }
+}
+
+// Split combine fused with the output projection (bf16 layers).  One
+// workgroup of 8 waves per (32 query tokens, head):
+//   1. per row: weights w_s = 2^(lse_s - max lse) over the splits that hold
+//      part of the row's sequence, and 1 / sum w_s (all lse loads of the
+//      block issued at once);
+//   2. o_lat rows = sum_s w_s O_s / sum w_s (normalised partials), rounded to
+//      bf16 into LDS; each thread keeps 2 splits x 8 rows of loads in flight;
+//   3. out^T = W_uv_h^T . o_lat^T on the matrix core, waves 0..3 taking value
+//      column blocks w, w + 4, ...; the B operand comes from LDS.
+// Splits past a row's sequence were never written: their weight is zero and
+// their (arbitrary) values are never added.
+constexpr int kCombThreads = 512;
+constexpr int kCombRowPad = 8;   // bf16 pad per LDS row of o_lat
+
+__global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
+    const float* __restrict__ opart, const float* __restrict__ lse, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seq_lens, const bf16* __restrict__ wuv, bf16* __restrict__ out,
+    int batch, int Tq, int H, int dv, int chunk, int S_max) {
+  constexpr int kDc = 512;
+  __shared__ CuStage cu_st;
+  __shared__ float w_s[kCombineMaxSplits][32];
+  __shared__ float inv_s[32];
+  __shared__ int sb_s[32];
+  __shared__ __attribute__((aligned(16))) bf16 ob[32][kDc + kCombRowPad];
+  const int32_t* cu = stage_cu(cu_st, cu_q, batch);
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % H, tb = blockIdx.x / H;
+  const int64_t rows_total = (int64_t)Tq * H;
+
+  if (tid < 32) {
+    const int t = tb * 32 + tid;
+    int sb = 0;
+    if (t < Tq) sb = (seq_lens[seq_of_token(cu, batch, t)] + chunk - 1) / chunk;
+    sb_s[tid] = sb;
+  }
+  __syncthreads();
+  constexpr int kLsePerThread = kCombineMaxSplits * 32 / kCombThreads;
+  {
+    float x[kLsePerThread];
+#pragma unroll
+    for (int u = 0; u < kLsePerThread; ++u) {
+      const int k = tid + kCombThreads * u, sp = k >> 5, r = k & 31;
+      x[u] = (sp < S_max && sp < sb_s[r]) ? lse[sp * rows_total + (int64_t)(tb * 32 + r) * H + h]
+                                          : -INFINITY;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma32(a[s], b[s], acc);
+    for (int u = 0; u < kLsePerThread; ++u) {
+      const int k = tid + kCombThreads * u;
+      if ((k >> 5) < S_max) w_s[k >> 5][k & 31] = x[u];
+    }
   }
+  __syncthreads();
+  if (tid < 32) {
+    float m = -INFINITY;
+    for (int sp = 0; sp < S_max; ++sp) m = fmaxf(m, w_s[sp][tid]);
+    float sum = 0.f;
+    for (int sp = 0; sp < S_max; ++sp) {
+      const float x = w_s[sp][tid];
+      const float w = (x == -INFINITY) ? 0.f : exp2f(x - m);
+      w_s[sp][tid] = w;
+      sum += w;
+    }
+    inv_s[tid] = sum > 0.f ? 1.f / sum : 0.f;
+  }
+  __syncthreads();
+
+  {
+    constexpr int kRows = 32 * (kDc / 4) / kCombThreads;   // rows per thread (8)
+    constexpr int kSp = 2;                                  // splits per round of loads
+    const int j = 4 * (tid & 127), r0 = tid >> 7;
+    f32x4 acc[kRows];
+    const float* src[kRows];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = m0 + acc_row32(r, lane);
-    if (t < Tq) out[((int64_t)t * H + h) * dv + v0 + (lane & 31)] = from_f32<bf16>(acc[r]);
+    for (int u = 0; u < kRows; ++u) {
+      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int t = min(tb * 32 + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
+      src[u] = opart + ((int64_t)t * H + h) * kDc + j;
+    }
+    for (int sp0 = 0; sp0 < S_max; sp0 += kSp) {
+      f32x4 v[kSp][kRows];
+#pragma unroll
+      for (int d = 0; d < kSp; ++d)
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+          if (sp0 + d < S_max)
+            v[d][u] = *reinterpret_cast<const f32x4*>(src[u] + (sp0 + d) * rows_total * kDc);
+#pragma unroll
+      for (int d = 0; d < kSp; ++d)
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+          const float w = (sp0 + d < S_max) ? w_s[sp0 + d][r0 + 4 * u] : 0.f;
+          if (w != 0.f) acc[u] += w * v[d][u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int r = r0 + 4 * u;
+      const float inv = inv_s[r];
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 o = {from_f32<bf16>(acc[u][0] * inv), from_f32<bf16>(acc[u][1] * inv),
+                  from_f32<bf16>(acc[u][2] * inv), from_f32<bf16>(acc[u][3] * inv)};
+      *reinterpret_cast<bf16x4*>(&ob[r][j]) = o;
+    }
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  if (wave >= 4) return;
+  const int t = tb * 32 + l32;
+  const bf16* wh = wuv + (int64_t)h * dv * kDc;
+  for (int vb = wave; vb < dv / 32; vb += 4) {
+    constexpr int NS = kDc / 16, kGrp = 8;
+    f32x16 acc = zero_f32x16();
+    bf16x8 a[2][kGrp];
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) {
+      a[0][u] = load_fragment(wh, vb, u, kDc, lane);
+      a[1][u] = load_fragment(wh, vb, kGrp + u, kDc, lane);
+    }
+#pragma unroll
+    for (int grp = 0; grp < NS / kGrp; ++grp) {
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        const int sk = grp * kGrp + u;
+        const bf16x8 bo = *reinterpret_cast<const bf16x8*>(&ob[l32][16 * sk + 8 * g]);
+        acc = mfma32(a[grp & 1][u], bo, acc);
+      }
+      if (grp + 2 < NS / kGrp) {
+#pragma unroll
+        for (int u = 0; u < kGrp; ++u) a[grp & 1][u] = load_fragment(wh, vb, (grp + 2) * kGrp + u, kDc, lane);
+      }
+    }
+    if (t < Tq) {
+      bf16* dst = out + ((int64_t)t * H + h) * dv + vb * 32 + 4 * g;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store_bf16x4(dst + 8 * r4, acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]);
+    }
   }
 }
 
@@ -148,32 +337,55 @@ __global__ void out_proj_f32_kernel(const float* __restrict__ olat, const float*
 
 }  // namespace
 
-void launch_absorb(int elem, const void* q, const void* wuk_p, void* abuf, const int32_t* cu_q,
-                   const int32_t* seq_lens, int batch, int Tq, int H, int dn, int dr, int dc,
-                   float base, hipStream_t st) {
+void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                   const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
+                   int dc, float base, const RopeFreq& freq, hipStream_t st) {
   if (elem == 2) {
-    dim3 grid((Tq + 31) / 32, dc / 32 + (32 * (dr / 2) + 63) / 64, H);
-    absorb_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk_p, (bf16*)abuf, cu_q,
-                                            seq_lens, batch, Tq, H, dn, dr, dc, base);
+    const int ntb = (Tq + 31) / 32;
+    const int gemm_blocks = ntb * H * (dc / 32 / kAbsorbJB);
+    const int TC = (max_q_len + kRopeTok - 1) / kRopeTok;
+    const int HG = (H + kRopeHeads - 1) / kRopeHeads;
+    const unsigned blocks = (unsigned)(gemm_blocks + batch * TC * HG);
+    switch (dn / 16) {
+#define MLA_ABSORB_CASE(NS)                                                                   \
+  case NS:                                                                                    \
+    absorb_bf16_kernel<NS><<<blocks, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk,          \
+                                                  (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, \
+                                                  gemm_blocks, TC, freq);                     \
+    break;
+      MLA_ABSORB_CASE(2) MLA_ABSORB_CASE(4) MLA_ABSORB_CASE(6) MLA_ABSORB_CASE(8)
+      MLA_ABSORB_CASE(10) MLA_ABSORB_CASE(12) MLA_ABSORB_CASE(14) MLA_ABSORB_CASE(16)
+#undef MLA_ABSORB_CASE
+      default: break;   // excluded by the config check
+    }
   } else {
     int64_t n = (int64_t)Tq * H * (dc + dr / 2);
     absorb_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-        (const float*)q, (const float*)wuk_p, (float*)abuf, cu_q, seq_lens, batch, Tq, H, dn, dr,
+        (const float*)q, (const float*)wuk, (float*)abuf, cu_q, seq_lens, batch, Tq, H, dn, dr,
         dc, base);
   }
 }
 
-void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
+void launch_out_proj(int elem, const void* olat, const void* wuv, void* out, int Tq, int H, int dc,
                      int dv, hipStream_t st) {
   if (elem == 2) {
-    dim3 grid((Tq + 31) / 32, dv / 32, H);
-    out_proj_bf16_kernel<<<grid, 64, 0, st>>>((const bf16*)olat, (const bf16*)wuv_p, (bf16*)out,
-                                               Tq, H, dc, dv);
+    const unsigned blocks = (unsigned)(((Tq + 31) / 32) * H * (dv / 32));
+    out_proj_bf16_kernel<<<blocks, 64, 0, st>>>((const bf16*)olat, (const bf16*)wuv, (bf16*)out, Tq,
+                                                H, dv);
   } else {
     int64_t n = (int64_t)Tq * H * dv;
     out_proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-        (const float*)olat, (const float*)wuv_p, (float*)out, Tq, H, dc, dv);
+        (const float*)olat, (const float*)wuv, (float*)out, Tq, H, dc, dv);
   }
+}
+
+void launch_combine_out(const SplitPlan& plan, const float* opart, const float* lse,
+                        const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
+                        int batch, int Tq, int H, int dv, hipStream_t st) {
+  const unsigned blocks = (unsigned)(((Tq + 31) / 32) * H);
+  combine_out_bf16_kernel<<<blocks, kCombThreads, 0, st>>>(opart, lse, cu_q, seq_lens, (const bf16*)wuv,
+                                                  (bf16*)out, batch, Tq, H, dv, plan.chunk,
+                                                  plan.S_max);
 }
 
 }  // namespace mla

@@ -4,11 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace mla {
 
 // ---- fold (pack) ---------------------------------------------------------
-// wdkv_t[n][d] = w_dkv[d][n]; wuk_p[h][j][i] = w_uk[j][h*dn+i];
-// wuv_p[h][v][j] = w_uv[j][h*dv+v].  elem = 2 (bf16) or 4 (fp32).
+// bf16 (elem 2): fragment-tiled wdkv (rows n, k = d), wuk[h] (rows j, k = i),
+// wuv[h] (rows v, k = j).  fp32 (elem 4): wdkv_t[n][d] = w_dkv[d][n];
+// wuk_p[h][j][i] = w_uk[j][h*dn+i]; wuv_p[h][v][j] = w_uv[j][h*dv+v].
 void launch_pack(int elem, const void* w_dkv, const void* w_uk, const void* w_uv, void* wdkv_t,
                  void* wuk_p, void* wuv_p, int d_model, int H, int dn, int dv, int dc, int dr,
                  hipStream_t st);
@@ -24,13 +27,13 @@ void launch_append_gemm_f32(const void* x, const void* wt, float* part, int M, i
 void launch_append_finish(int elem, const float* part, int ksplits, int T, const int32_t* cu_new,
                           const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
                           int batch, void* cache, int page_size, int dc, int dr, float base,
-                          hipStream_t st);
+                          const RopeFreq& freq, hipStream_t st);
 
 // ---- per-head GEMMs --------------------------------------------------------
 // abuf[t][h][0:dc] = W_uk_h q_nope[t][h]; abuf[t][h][dc:] = rot(q_rope, pos_t)
-void launch_absorb(int elem, const void* q, const void* wuk_p, void* abuf, const int32_t* cu_q,
-                   const int32_t* seq_lens, int batch, int Tq, int H, int dn, int dr, int dc,
-                   float base, hipStream_t st);
+void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                   const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
+                   int dc, float base, const RopeFreq& freq, hipStream_t st);
 // out[t][h][v] = sum_j olat[t][h][j] * wuv_p[h][v][j]
 void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
                      int dv, hipStream_t st);
@@ -46,6 +49,12 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
                     float scale, float* opart, float* lse, hipStream_t st);
+// out[t][h][:] = (LSE-weighted merge of the split partials) . W_uv_h, one
+// workgroup per (32 query tokens, head); bf16 layers, at most kCombineMaxSplits.
+constexpr int kCombineMaxSplits = 64;
+void launch_combine_out(const SplitPlan& plan, const float* opart, const float* lse,
+                        const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
+                        int batch, int Tq, int H, int dv, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

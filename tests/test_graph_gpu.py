@@ -1,0 +1,57 @@
+"""The append + decode step captured as a HIP graph (how a serving loop, and
+bench.py, run it): every replay must reproduce the eager result bit for bit,
+with ordinary eager work and synchronisations between replays."""
+import pytest
+import torch
+
+from mla_synth import workload
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_harness import GpuCase  # noqa: E402
+
+
+def test_graph_replay_matches_eager():
+    wl = workload("dsv2_ragged_paged_256", name="graph", batch=5, max_prefix=300)
+    print(f"[graph] case {wl.name} B={wl.batch}", flush=True)
+    case = GpuCase(wl)
+    mla = case.mla
+    s = wl.shape
+    Tq = case.q.shape[0]
+    ws = torch.empty(mla.mla_decode_workspace_bytes(case.layer, wl.batch, Tq, case.max_q_len,
+                                                    case.max_seq_len, 128), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(max(1, mla.mla_append_workspace_bytes(case.layer, Tq)), dtype=torch.uint8, device="cuda")
+
+    def step(out, stream=None):
+        mla.mla_append_latent(case.layer, case.x_new_dev, case.cu_q, case.prefix_dev, case.page_table, case.cache,
+                              workspace=aws, stream=stream)
+        mla.mla_decode(case.layer, case.q_dev, case.cu_q, case.seq_lens, case.page_table, case.cache, out,
+                       case.max_q_len, case.max_seq_len, kv_chunk=128, workspace=ws, stream=stream)
+
+    eager = torch.empty((Tq, s.H, s.d_v), dtype=case.dt, device="cuda")
+    step(eager)
+    torch.cuda.synchronize()
+
+    out_g = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(out_g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+
+    other = torch.empty_like(eager)
+    for rep in range(3):
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), f"graph replay {rep} differs from the eager result"
+        step(other)                     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    print("[graph] 3 replays identical to eager", flush=True)

@@ -148,3 +148,15 @@ def test_split_invariance():
     a, b, c = (o.float().cpu().numpy() for o in (out_a, out_b, out_c))
     scale = np.abs(a).max()
     assert np.abs(a - b).max() / scale < 1e-2 and np.abs(a - c).max() / scale < 1e-2
+
+
+def test_many_splits_separate_combine():
+    """More splits than the fused combine stages (64): the separate combine and
+    output-projection kernels run instead; sampled heads against the oracle."""
+    wl = workload("dsv2_b32_ctx4096", name="many_splits", shape=SMALL_DSV2, batch=2, fixed_prefix=4500)
+    case, out = _run(wl, kv_chunk=64)
+    heads = [0, 37, 127]
+    _check(case, out, heads=heads, tag="many_splits chunk=64 (71 splits)")
+    out_fused = case.decode(kv_chunk=128)     # 36 splits: fused combine + projection
+    torch.cuda.synchronize()
+    _check(case, out_fused, heads=heads, tag="many_splits chunk=128 (36 splits)")
