@@ -26,6 +26,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 GPU"
+
+# HBM bytes per split-KV launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled
+# by the same counters on a 256 MiB device copy (x2.000 and x1.000), keyed by
+# the kernel source they were taken on and the workload (profiles/ holds the
+# runs).  A changed kernel reports null until counters are taken again.
+MEASURED_TRAFFIC = {
+    ("efda8d2e4fd036e2", "dsv2_b32_ctx4096"): {"fetch_bytes": 156039091, "write_bytes": 70415056},
+}
+
+
+def splitkv_source_id():
+    import hashlib
+    path = os.path.join(ROOT, "mla_compressed_latent_amd", "csrc", "splitkv.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, published
 
@@ -261,6 +276,8 @@ def main():
     achieved = latent_bytes / attend_s / 1e9
     # scores (K = d_c + d_rope) and value sums (K = d_c) per query row and cached token
     q_lens = wl.q_lens()
+    traffic = MEASURED_TRAFFIC.get((splitkv_source_id(), wl.name))
+    traffic_bytes = None if traffic is None else traffic["fetch_bytes"] + traffic["write_bytes"]
     flops = 2.0 * s.H * (2 * s.d_c + s.d_rope) * float(
         sum(int(L) * int(lq) for L, lq in zip(st["seq_lens_np"], q_lens)))
     res = {
@@ -289,7 +306,8 @@ def main():
                      "combine_and_output": phase[3] * 1e3},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_bytes,
+            "traffic_detail": traffic,
             "kernel": "split-KV attention (MLA_PHASE_ATTEND)",
             "algorithmic_bytes_per_launch": latent_bytes,
             "mfma_tflops": flops / attend_s / 1e12,
