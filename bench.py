@@ -32,15 +32,21 @@ METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("efda8d2e4fd036e2", "dsv2_b32_ctx4096"): {"fetch_bytes": 156039091, "write_bytes": 70415056},
 }
 
 
+ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip")
+
+
 def splitkv_source_id():
+    """Hash of the attention kernels' sources (the counters below are valid
+    for exactly this code)."""
     import hashlib
-    path = os.path.join(ROOT, "mla_compressed_latent_amd", "csrc", "splitkv.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, "mla_compressed_latent_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, published
 

@@ -98,8 +98,8 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
   const int H = L->cfg.num_attention_heads;
   const int rows = max_q_len * H;
   if (L->elem == 2) {
-    if (rows >= 128) { p->NB = 4; p->RQ = (rows + 127) / 128; }
-    else if (rows > 32) { p->NB = 2; p->RQ = (rows + 63) / 64; }
+    // more than 32 rows: 64-row workgroups of eight waves; else one 32-row block
+    if (rows > 32) { p->NB = 8; p->RQ = (rows + 63) / 64; }
     else { p->NB = 1; p->RQ = 1; }
   } else {
     p->NB = 1;

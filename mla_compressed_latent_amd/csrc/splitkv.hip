@@ -29,233 +29,16 @@
 //     load (ds_read_b64_tr_b16);
 //   * the score waves work one tile ahead of the value waves, so the two kinds
 //     of matrix work overlap; one barrier per tile.
+#include "attn_tile.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mla {
 namespace {
 
-constexpr int kDC = 512, kDR = 64, kD = kDC + kDR;
-constexpr int kChunks = kD / 8;              // 16-byte chunks per cached row (72)
-constexpr int kTileTok = 32;
-constexpr int kTileBytes = kTileTok * kD * 2;
-constexpr int kDmaPerWave = kTileBytes / 16 / 64 / 4;   // 9 wave-wide DMAs per wave per tile
-constexpr float kRescaleThreshold = 8.0f;    // log2 units: P may grow to 2^8 before rescale
-constexpr int kMaxChunkTokens = 8192;         // largest split the attention kernel accepts
-constexpr int kMaxChunkPages = kMaxChunkTokens / 64;
-
 constexpr int kNBuf = 4;                      // tiles resident in LDS (3 in flight)
 constexpr int kQkRing = 3;                    // score-operand read groups in flight
 constexpr int kPvRing = 6;                    // value-operand reads in flight
-
-// Chunk swizzle: 16-byte chunk c of token t is stored at position
-// c ^ swz(t) of the token's LDS row (the XOR stays inside c's aligned group of
-// 8, so the 72 chunks of a row stay in the row).  LDS on gfx950 has 64 banks;
-// swz mixes token bits 1..3 with bit 4 so that the score-operand reads (one
-// chunk of 32 consecutive tokens per half wave) spread over all banks; the
-// transposing value-operand reads stay conflict-light too (measured).
-__device__ __forceinline__ int swz(int t) { return ((t >> 1) ^ (t >> 4)) & 7; }
-
-typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
-// (i mod 4) of the 8-byte words addressed by lanes 4j + i/4, j = 0..3.
-__device__ __forceinline__ v4bf16 ds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) v4bf16*)(const __attribute__((address_space(3))) char*)p);
-}
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0],
-// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
-  if (ahead <= 0) wait_vmcnt<0>();
-  else if (ahead == 1) wait_vmcnt<kDmaPerWave>();
-  else if (ahead == 2) wait_vmcnt<2 * kDmaPerWave>();
-  else wait_vmcnt<3 * kDmaPerWave>();
-}
-
-// One wave-wide 16-byte-per-lane copy HBM -> LDS: lane i's 16 bytes from
-// gbase + voff land at LDS byte address lds_addr + 16 i.  Issued as inline
-// assembly so that the only waits on it are the explicit vmcnt waits.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %0"
-      :
-      : "s"(gbase), "v"(voff), "s"(lds_addr)
-      : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Score MFMAs with the accumulator in VGPRs.  The compiler keeps every other
-// matrix-core accumulator of this kernel (the 256 registers of O) in AGPRs;
-// issuing the score chain as assembly keeps its 16 accumulators out of that
-// file.  Back-to-back accumulation into the same registers needs no wait
-// states; the last block ends with 32 wait states so that ordinary vector
-// instructions may read the result (more than the pass count plus margin
-// the hardware requires); each block starts with two wait states in case the
-// compiler has just moved an operand into place with a vector ALU op.
-__device__ __forceinline__ void qk_mfma4(f32x16& acc, const bf16x8& a0, const bf16x8& b0,
-                                         const bf16x8& a1, const bf16x8& b1, const bf16x8& a2,
-                                         const bf16x8& b2, const bf16x8& a3, const bf16x8& b3) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %8, %0"
-      : "+v"(acc)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
-}
-
-__device__ __forceinline__ void qk_mfma4_first(f32x16& acc, const bf16x8& a0, const bf16x8& b0,
-                                               const bf16x8& a1, const bf16x8& b1,
-                                               const bf16x8& a2, const bf16x8& b2,
-                                               const bf16x8& a3, const bf16x8& b3) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %8, %0"
-      : "=&v"(acc)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
-}
-
-__device__ __forceinline__ void qk_mfma4_last(f32x16& acc, const bf16x8& a0, const bf16x8& b0,
-                                              const bf16x8& a1, const bf16x8& b1,
-                                              const bf16x8& a2, const bf16x8& b2,
-                                              const bf16x8& a3, const bf16x8& b3) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %4, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %8, %0\n\t"
-      "s_nop 15\n\t"
-      "s_nop 15"
-      : "+v"(acc)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
-}
-
-// Value MFMAs, accumulators pinned to AGPRs: one A operand (a transposed
-// tile fragment) against the probability fragments of NB row blocks.  Starts
-// with two wait states (the A operand was just assembled by vector ALU ops).
-template <int NB>
-__device__ __forceinline__ void pv_mfma(f32x16 (&o)[NB], const bf16x8& a, const bf16x8 (&p)[NB]) {
-  if constexpr (NB == 1) {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-        : "+a"(o[0])
-        : "v"(a), "v"(p[0]));
-  } else if constexpr (NB == 2) {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
-        : "+a"(o[0]), "+a"(o[1])
-        : "v"(a), "v"(p[0]), "v"(p[1]));
-  } else {
-    static_assert(NB == 4, "row blocks");
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %4, %5, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %2, %4, %7, %2\n\t"
-        "v_mfma_f32_32x32x16_bf16 %3, %4, %8, %3"
-        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3])
-        : "v"(a), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
-  }
-}
-
-// 32 wait states after the last value MFMA before the accumulators are read
-// by ordinary instructions; taking them as operands orders the reads after.
-template <int NB, int NDB>
-__device__ __forceinline__ void pv_drain(f32x16 (&o)[NDB][NB]) {
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    if constexpr (NB == 1) {
-      asm volatile("s_nop 7" : "+a"(o[db][0]));
-    } else if constexpr (NB == 2) {
-      asm volatile("s_nop 7" : "+a"(o[db][0]), "+a"(o[db][1]));
-    } else {
-      asm volatile("s_nop 7" : "+a"(o[db][0]), "+a"(o[db][1]), "+a"(o[db][2]), "+a"(o[db][3]));
-    }
-  }
-}
-
-// Both halves of a wave hold the same 32 rows (acc_row32: lane l and l ^ 32
-// hold different tokens of row l % 32).  permlane32_swap hands each lane its
-// partner's value without going through LDS; r[0] is the lower half's value
-// and r[1] the upper half's in every lane, so both halves combine them in the
-// same order and agree bit for bit.
-__device__ __forceinline__ float2 lane_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Online softmax over one 32-token tile held in the score accumulator
-// (row l % 32, token tok0 + acc_row32(r, l)).  Scores are scaled into log2
-// units; tokens past the row's last visible position `limit` are masked
-// (only needed when the tile reaches past the smallest limit of the block).
-// The running max moves lazily: only when a score exceeds it by more than
-// kRescaleThreshold, so rescaling O is rare and P stays below 2^threshold.
-// Returns the rescale factor alpha for O; writes the bf16 probabilities as the
-// two k-step fragments of the value MFMA.
-__device__ __forceinline__ float softmax_tile(f32x16& acc, bool masked, int tok0, int limit,
-                                              float scale_log2e, float& m_run, float& l_run,
-                                              bf16x8& pf0, bf16x8& pf1) {
-  const int lane = threadIdx.x & 63;
-  float tmax = -INFINITY;
-  if (masked) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = tok0 + acc_row32(r, lane);
-      acc[r] = (tok <= limit) ? acc[r] * scale_log2e : -INFINITY;
-      tmax = fmaxf(tmax, acc[r]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc[r] *= scale_log2e;
-      tmax = fmaxf(tmax, acc[r]);
-    }
-  }
-  {
-    const float2 h = lane_halves(tmax);
-    tmax = fmaxf(h.x, h.y);
-  }
-  const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
-  const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-  const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-  float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    // probabilities below 2^-126 of the running max flush to zero
-    const float pv = __builtin_amdgcn_exp2f(acc[r] - m_ref);
-    rs += pv;
-    if (r < 8) pf0[r] = from_f32<bf16>(pv);
-    else pf1[r - 8] = from_f32<bf16>(pv);
-  }
-  {
-    const float2 h = lane_halves(rs);
-    rs = h.x + h.y;
-  }
-  l_run = l_run * alpha + rs;
-  m_run = m_new;
-  return alpha;
-}
 
 template <int NB>
 __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
@@ -916,6 +699,10 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
   if (elem == 2) {
     const int nblocks = batch * plan.S_max * plan.RQ;
     switch (plan.NB) {
+      case 8:
+        launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
+                          page_size, scale, opart, lse, st);
+        break;
       case 4:
         splitkv_bf16_rows128_kernel<<<nblocks, 256, 0, st>>>(
             (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
