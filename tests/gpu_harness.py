@@ -64,12 +64,14 @@ class GpuCase:
         self.prefix_dev = i32(self.prefix)
 
     def _fill_prefix(self, seq_group):
+        import concurrent.futures as cf
         wl, mla = self.wl, self.mla
         B = wl.batch
+        pool = cf.ThreadPoolExecutor(max_workers=8)   # the generator's draws release the GIL
         if wl.prefix_source == "hidden":
             for b0 in range(0, B, seq_group):
                 bs = list(range(b0, min(B, b0 + seq_group)))
-                xs = [wl.prefix_hidden(b) for b in bs]
+                xs = list(pool.map(wl.prefix_hidden, bs))
                 lens = np.array([x.shape[0] for x in xs], dtype=np.int64)
                 cu = np.zeros(B + 1, dtype=np.int64)
                 for j, b in enumerate(bs):
@@ -80,14 +82,18 @@ class GpuCase:
                 del x
         else:
             ps = wl.shape.page_size
+            futs = {b: pool.submit(wl.prefix_latent, b) for b in range(min(B, 16))}
             for b in range(B):
-                rows = wl.prefix_latent(b)
+                rows = futs.pop(b).result()
+                if b + 16 < B:
+                    futs[b + 16] = pool.submit(wl.prefix_latent, b + 16)
                 rd = to_dev(rows, self.dt)
                 P = rows.shape[0]
                 for p0 in range(0, P, ps):
                     page = int(self.table_np[b, p0 // ps])
                     n = min(ps, P - p0)
                     self.cache[page, :n] = rd[p0:p0 + n]
+        pool.shutdown()
         torch.cuda.synchronize()
 
     def append_new(self, stream=None):
