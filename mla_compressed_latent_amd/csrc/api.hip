@@ -307,7 +307,7 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
   if (phases & MLA_PHASE_ABSORB)
     mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, max_q_len, H,
                        c.qk_nope_head_dim, c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, L->freq,
-                       st);
+                       L->scale * 1.4426950408889634f, st);
   if (phases & MLA_PHASE_ATTEND)
     mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse, st);

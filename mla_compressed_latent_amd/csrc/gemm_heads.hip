@@ -25,7 +25,7 @@ __device__ __forceinline__ int query_position(const int32_t* __restrict__ cu_q,
   return seq_lens[b] - (cu_q[b + 1] - cu_q[b]) + (t - cu_q[b]);
 }
 
-constexpr int kAbsorbJB = 2;      // 32-column blocks of q_lat per wave
+constexpr int kAbsorbTokBlocks = 8;   // 32-token blocks one absorb wave handles
 constexpr int kRopeTok = 4;       // query tokens per rope workgroup
 constexpr int kRopeHeads = 16;    // heads per rope workgroup
 
@@ -37,7 +37,12 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float 
 
 // q_lat^T block = W_uk_h^T (32 latent rows x d_nope) . q_nope^T (d_nope x 32
 // tokens): the folded weight is the A operand, streamed as contiguous
-// fragments; the 32 query rows are the B operand.  One wave per (32-token
+// fragments; the 32 query rows are the B operand.  One wave per (head, 128
+// latent columns, up to kAbsorbTokBlocks token blocks): its weight fragments
+// stay in registers while the token blocks stream past, so W_uk is read
+// about once per step however many query tokens there are.  The stored score operand
+// (q_lat and the rotated rope part) is pre-multiplied by qscale = softmax
+// scale * log2(e), so the attention kernel's scores come out in log2 units.  One wave per (32-token
 // block, head, kAbsorbJB column blocks); each lane stores 4 consecutive
 // latent values of one token.
 //
@@ -49,7 +54,7 @@ template <int NS>   // d_nope / 16
 __global__ __launch_bounds__(64) void absorb_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
-    int dc, int gemm_blocks, int TC, const RopeFreq freq) {
+    int dc, int gemm_blocks, int TC, const RopeFreq freq, float qscale) {
   constexpr int dn = NS * 16;
   const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
   if ((int)blockIdx.x >= gemm_blocks) {
@@ -76,36 +81,56 @@ __global__ __launch_bounds__(64) void absorb_bf16_kernel(
         if (h >= H) continue;
         const float x0 = __uint_as_float(v[m] << 16), x1 = __uint_as_float(v[m] & 0xffff0000u);
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 r = {from_f32<bf16>(x0 * c - x1 * sn), from_f32<bf16>(x0 * sn + x1 * c)};
+        bf16x2 r = {from_f32<bf16>((x0 * c - x1 * sn) * qscale), from_f32<bf16>((x0 * sn + x1 * c) * qscale)};
         *reinterpret_cast<bf16x2*>(abuf + (t * H + h) * D + dc + 2 * p) = r;
       }
     }
     return;
   }
-  const int JG = dc / 32 / kAbsorbJB;
+  constexpr int JB = NS <= 8 ? 4 : 2;   // 32-column blocks per wave, held in registers
+  const int JG = dc / 32 / JB;
+  const int ntb = (Tq + 31) / 32;
+  const int TBW = min(ntb, kAbsorbTokBlocks);   // token blocks per wave
   const int id = blockIdx.x;
-  const int jg = id % JG, h = (id / JG) % H, tb = id / (JG * H);
+  const int jg = id % JG, h = (id / JG) % H, tbg = id / (JG * H);
   const int dq = dn + dr, D = dc + dr;
-  const int t = tb * 32 + l32;
-  const bf16* qrow = q + ((int64_t)min(t, Tq - 1) * H + h) * dq + 8 * g;
   const bf16* wh = wuk + (int64_t)h * dc * dn;
-  bf16x8 bq[NS], wa[kAbsorbJB][NS];
+  bf16x8 wa[JB][NS];
 #pragma unroll
-  for (int jb = 0; jb < kAbsorbJB; ++jb)
+  for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) wa[jb][s] = load_fragment(wh, jg * kAbsorbJB + jb, s, dn, lane);
+    for (int s = 0; s < NS; ++s) wa[jb][s] = load_fragment(wh, jg * JB + jb, s, dn, lane);
+  const int tb_end = min(ntb, (tbg + 1) * TBW);
+  auto load_q = [&](int tb, bf16x8 (&dst)[NS]) {
+    const bf16* qrow = q + ((int64_t)min(tb * 32 + l32, Tq - 1) * H + h) * dq + 8 * g;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) bq[s] = load_bf16x8(qrow + 16 * s);
+    for (int s = 0; s < NS; ++s) dst[s] = load_bf16x8(qrow + 16 * s);
+  };
+  auto compute = [&](int tb, const bf16x8 (&bq)[NS]) {
+    const int t = tb * 32 + l32;
 #pragma unroll
-  for (int jb = 0; jb < kAbsorbJB; ++jb) {
-    f32x16 acc = zero_f32x16();
+    for (int jb = 0; jb < JB; ++jb) {
+      f32x16 acc = zero_f32x16();
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc = mfma32(wa[jb][s], bq[s], acc);
-    if (t < Tq) {
-      bf16* dst = abuf + ((int64_t)t * H + h) * D + (jg * kAbsorbJB + jb) * 32 + 4 * g;
+      for (int s = 0; s < NS; ++s) acc = mfma32(wa[jb][s], bq[s], acc);
+      if (t < Tq) {
+        bf16* dst = abuf + ((int64_t)t * H + h) * D + (jg * JB + jb) * 32 + 4 * g;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        store_bf16x4(dst + 8 * r4, acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]);
+        for (int r4 = 0; r4 < 4; ++r4)
+          store_bf16x4(dst + 8 * r4, acc[4 * r4] * qscale, acc[4 * r4 + 1] * qscale,
+                       acc[4 * r4 + 2] * qscale, acc[4 * r4 + 3] * qscale);
+      }
+    }
+  };
+  // ping-pong over two statically indexed query buffers
+  bf16x8 qa[NS], qb[NS];
+  load_q(tbg * TBW, qa);
+  for (int tb = tbg * TBW; tb < tb_end; tb += 2) {
+    if (tb + 1 < tb_end) load_q(tb + 1, qb);
+    compute(tb, qa);
+    if (tb + 1 < tb_end) {
+      if (tb + 2 < tb_end) load_q(tb + 2, qa);
+      compute(tb + 1, qb);
     }
   }
 }
@@ -228,19 +253,27 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       const int t = min(tb * 32 + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
       src[u] = opart + ((int64_t)t * H + h) * kDc + j;
     }
-    for (int sp0 = 0; sp0 < S_max; sp0 += kSp) {
+    // splits a row's sequence has (the rows of one thread are the same for
+    // the whole wave, so these guards never diverge)
+    int sb[kRows], smax = 0;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      sb[u] = sb_s[r0 + 4 * u];
+      smax = max(smax, sb[u]);
+    }
+    for (int sp0 = 0; sp0 < smax; sp0 += kSp) {
       f32x4 v[kSp][kRows];
 #pragma unroll
       for (int d = 0; d < kSp; ++d)
 #pragma unroll
         for (int u = 0; u < kRows; ++u)
-          if (sp0 + d < S_max)
+          if (sp0 + d < sb[u])
             v[d][u] = *reinterpret_cast<const f32x4*>(src[u] + (sp0 + d) * rows_total * kDc);
 #pragma unroll
       for (int d = 0; d < kSp; ++d)
 #pragma unroll
         for (int u = 0; u < kRows; ++u) {
-          const float w = (sp0 + d < S_max) ? w_s[sp0 + d][r0 + 4 * u] : 0.f;
+          const float w = (sp0 + d < sb[u]) ? w_s[sp0 + d][r0 + 4 * u] : 0.f;
           if (w != 0.f) acc[u] += w * v[d][u];
         }
     }
@@ -339,10 +372,12 @@ __global__ void out_proj_f32_kernel(const float* __restrict__ olat, const float*
 
 void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
                    const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
-                   int dc, float base, const RopeFreq& freq, hipStream_t st) {
+                   int dc, float base, const RopeFreq& freq, float qscale, hipStream_t st) {
   if (elem == 2) {
     const int ntb = (Tq + 31) / 32;
-    const int gemm_blocks = ntb * H * (dc / 32 / kAbsorbJB);
+    const int tbw = ntb < kAbsorbTokBlocks ? ntb : kAbsorbTokBlocks;
+    const int jb = dn / 16 <= 8 ? 4 : 2;
+    const int gemm_blocks = ((ntb + tbw - 1) / tbw) * H * (dc / 32 / jb);
     const int TC = (max_q_len + kRopeTok - 1) / kRopeTok;
     const int HG = (H + kRopeHeads - 1) / kRopeHeads;
     const unsigned blocks = (unsigned)(gemm_blocks + batch * TC * HG);
@@ -351,7 +386,7 @@ void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const i
   case NS:                                                                                    \
     absorb_bf16_kernel<NS><<<blocks, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk,          \
                                                   (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, \
-                                                  gemm_blocks, TC, freq);                     \
+                                                  gemm_blocks, TC, freq, qscale);             \
     break;
       MLA_ABSORB_CASE(2) MLA_ABSORB_CASE(4) MLA_ABSORB_CASE(6) MLA_ABSORB_CASE(8)
       MLA_ABSORB_CASE(10) MLA_ABSORB_CASE(12) MLA_ABSORB_CASE(14) MLA_ABSORB_CASE(16)

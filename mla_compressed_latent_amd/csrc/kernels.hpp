@@ -30,10 +30,11 @@ void launch_append_finish(int elem, const float* part, int ksplits, int T, const
                           const RopeFreq& freq, hipStream_t st);
 
 // ---- per-head GEMMs --------------------------------------------------------
-// abuf[t][h][0:dc] = W_uk_h q_nope[t][h]; abuf[t][h][dc:] = rot(q_rope, pos_t)
+// abuf[t][h][0:dc] = W_uk_h q_nope[t][h]; abuf[t][h][dc:] = rot(q_rope, pos_t);
+// bf16 layers store both parts multiplied by qscale (softmax scale * log2 e).
 void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
                    const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
-                   int dc, float base, const RopeFreq& freq, hipStream_t st);
+                   int dc, float base, const RopeFreq& freq, float qscale, hipStream_t st);
 // out[t][h][v] = sum_j olat[t][h][j] * wuv_p[h][v][j]
 void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
                      int dv, hipStream_t st);
@@ -58,8 +59,8 @@ void launch_combine_out(const SplitPlan& plan, const float* opart, const float* 
 // 64 query rows per workgroup, eight waves (bf16 layers, plan.NB == 8).
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                       int max_pages, int batch, int Tq, int H, int page_size, float scale,
-                       float* opart, float* lse, hipStream_t st);
+                       int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                       float* lse, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

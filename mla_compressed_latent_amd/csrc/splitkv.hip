@@ -695,13 +695,14 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
                     float scale, float* opart, float* lse, hipStream_t st) {
-  const float scale_log2e = scale * 1.4426950408889634f;
+  // bf16 layers: the absorbed queries already carry scale * log2(e)
+  const float scale_log2e = elem == 2 ? 1.f : scale * 1.4426950408889634f;
   if (elem == 2) {
     const int nblocks = batch * plan.S_max * plan.RQ;
     switch (plan.NB) {
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                          page_size, scale, opart, lse, st);
+                          page_size, opart, lse, st);
         break;
       case 4:
         splitkv_bf16_rows128_kernel<<<nblocks, 256, 0, st>>>(

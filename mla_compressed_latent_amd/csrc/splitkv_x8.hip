@@ -39,13 +39,22 @@ constexpr int kX8Dma = kTileBytes / 16 / 64 / 4;        // 9 copies per value wa
 constexpr int kQSteps = kD / 32;                        // 18 k-steps of the 16x16x32 score product
 constexpr int kX8Ring = 6;                              // k-steps of tile reads in flight (2 reads each)
 
+// max of two scores (finite or -inf, never NaN here): the bare instruction,
+// without the canonicalising moves fmaxf adds for values it cannot prove
+// canonical
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
 // in the same order in every lane.
 __device__ __forceinline__ float quad_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float quad_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -85,7 +94,7 @@ __device__ __forceinline__ void qk16_drain(f32x4& c0, f32x4& c1) {
 __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
     const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
-    int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
+    int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
     float* __restrict__ opart, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kX8Buf][kTileTok * kD];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][4][64];   // [tile parity][2 rb + ks][lane]
@@ -186,43 +195,33 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       // (token 16 m + 4 G + i of acc[m][i])
       const int tok0 = tok_begin + it * kTileTok;
       const bool masked = tok0 + kTileTok - 1 > L - Lq;
-      float tmax = -INFINITY;
+      // scores are already in log2 units (the absorbed queries carry the scale)
       if (masked) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = tok0 + 16 * m + 4 * G + i > lim ? -INFINITY : acc[m][i] * scale_log2e;
-            acc[m][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[m][i] *= scale_log2e;
-            tmax = fmaxf(tmax, acc[m][i]);
-          }
+          for (int i = 0; i < 4; ++i)
+            if (tok0 + 16 * m + 4 * G + i > lim) acc[m][i] = -INFINITY;
       }
+      float tmax = max_raw(max_raw(max_raw(acc[0][0], acc[0][1]), max_raw(acc[0][2], acc[0][3])),
+                           max_raw(max_raw(acc[1][0], acc[1][1]), max_raw(acc[1][2], acc[1][3])));
       tmax = quad_max(tmax);
       const float m_new = (tmax > m_run + kRescaleThreshold) ? tmax : m_run;
       const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      float rs = 0.f;
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      float p[2][4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[m][i] = __builtin_amdgcn_exp2f(acc[m][i] - m_ref);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(acc[m][i] - m_ref);
-          rs += p[i];
-        }
-        bf16x4 pv = {from_f32<bf16>(p[0]), from_f32<bf16>(p[1]), from_f32<bf16>(p[2]),
-                     from_f32<bf16>(p[3])};
+        bf16x4 pv = {from_f32<bf16>(p[m][0]), from_f32<bf16>(p[m][1]), from_f32<bf16>(p[m][2]),
+                     from_f32<bf16>(p[m][3])};
         *reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&pbuf[it & 1][fb + m][lp]) + 8 * (G & 1)) = pv;
       }
+      float rs = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
       rs = quad_sum(rs);
       l_run = l_run * alpha + rs;
       m_run = m_new;
@@ -312,8 +311,9 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         else wait_vmcnt<0>();
       }
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
-      // LDS reads first (probabilities, rescale factors, value operands of the
-      // first half), so their latency runs under the copy issue below
+      if (it + 2 < ntiles) issue_tile(it + 2);
+      // then the LDS reads (probabilities, rescale factors, value operands of
+      // the first half), whose latency runs under the tail-zeroing below
       const int pt = (it - 1) & 1;
       const char* tb = reinterpret_cast<const char*>(&tiles[(it + kX8Buf - 1) % kX8Buf][0]);
       bf16x8 pb[2][2];
@@ -328,7 +328,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         for (int rb = 0; rb < 2; ++rb) al[rb] = alpha_s[pt][32 * rb + l32];
         load_pv_operands(tb, 0, f0);
       }
-      if (it + 2 < ntiles) issue_tile(it + 2);
       if (it < ntiles) {
         // rows past the sequence's end hold whatever the page held; zero their
         // value columns so that zero probabilities never meet a NaN
@@ -386,13 +385,12 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
 
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                       int max_pages, int batch, int Tq, int H, int page_size, float scale,
-                       float* opart, float* lse, hipStream_t st) {
-  const float scale_log2e = scale * 1.4426950408889634f;
+                       int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                       float* lse, hipStream_t st) {
   const int nblocks = batch * plan.S_max * plan.RQ;
   splitkv_bf16_x8_kernel<<<nblocks, 512, 0, st>>>(
       (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-      page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
+      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
 }
 
 }  // namespace mla
