@@ -35,7 +35,7 @@ MEASURED_TRAFFIC = {
 }
 
 
-ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip")
+ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip", "splitkv_x8p.hip")
 
 
 def splitkv_source_id():

@@ -228,5 +228,57 @@ __device__ __forceinline__ float softmax_tile(f32x16& acc, bool masked, int tok0
   return alpha;
 }
 
+// max of two scores (finite or -inf, never NaN here): the bare instruction,
+// without the canonicalising moves fmaxf adds for values it cannot prove
+// canonical
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// in the same order in every lane.
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two score MFMAs (both 16-token halves of the tile) against one query
+// fragment held in AGPRs.  Starts with two wait states (an A operand may have
+// been moved into place by a vector instruction).
+__device__ __forceinline__ void qk16x2(f32x4& c0, f32x4& c1, const bf16x8& a0, const bf16x8& a1,
+                                       const bf16x8& b) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(a1), "a"(b));
+}
+__device__ __forceinline__ void qk16x2_first(f32x4& c0, f32x4& c1, const bf16x8& a0,
+                                             const bf16x8& a1, const bf16x8& b) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, 0"
+      : "=&v"(c0), "=&v"(c1)
+      : "v"(a0), "v"(a1), "a"(b));
+}
+// 16 wait states after the last score MFMA before vector instructions read
+// the accumulators (more than the pass count plus margin the hardware needs);
+// taking them as operands orders the reads after.
+__device__ __forceinline__ void qk16_drain(f32x4& c0, f32x4& c1) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+
 }  // namespace
 }  // namespace mla

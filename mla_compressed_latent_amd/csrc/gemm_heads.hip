@@ -176,58 +176,65 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 }
 
 // Split combine fused with the output projection (bf16 layers).  One
-// workgroup of 8 waves per (32 query tokens, head):
+// workgroup of 8 waves per (TB query tokens, head), TB in {32, 16, 8, 4}
+// chosen by the launcher so that the grid covers the chip:
 //   1. per row: weights w_s = 2^(lse_s - max lse) over the splits that hold
 //      part of the row's sequence, and 1 / sum w_s (all lse loads of the
 //      block issued at once);
 //   2. o_lat rows = sum_s w_s O_s / sum w_s (normalised partials), rounded to
-//      bf16 into LDS; each thread keeps 2 splits x 8 rows of loads in flight;
+//      bf16 into LDS; each thread keeps 16 row-split loads of 16 bytes in
+//      flight;
 //   3. out^T = W_uv_h^T . o_lat^T on the matrix core, waves 0..3 taking value
-//      column blocks w, w + 4, ...; the B operand comes from LDS.
+//      column blocks w, w + 4, ...; the B operand comes from LDS (columns past
+//      TB hold stale values and are never stored).
 // Splits past a row's sequence were never written: their weight is zero and
 // their (arbitrary) values are never added.
 constexpr int kCombThreads = 512;
 constexpr int kCombRowPad = 8;   // bf16 pad per LDS row of o_lat
 
+template <int TB>
 __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
     const float* __restrict__ opart, const float* __restrict__ lse, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const bf16* __restrict__ wuv, bf16* __restrict__ out,
     int batch, int Tq, int H, int dv, int chunk, int S_max) {
+  static_assert(TB == 32 || TB == 16 || TB == 8 || TB == 4, "token block");
   constexpr int kDc = 512;
   __shared__ CuStage cu_st;
-  __shared__ float w_s[kCombineMaxSplits][32];
-  __shared__ float inv_s[32];
-  __shared__ int sb_s[32];
+  __shared__ float w_s[kCombineMaxSplits][TB];
+  __shared__ float inv_s[TB];
+  __shared__ int sb_s[TB];
   __shared__ __attribute__((aligned(16))) bf16 ob[32][kDc + kCombRowPad];
   const int32_t* cu = stage_cu(cu_st, cu_q, batch);
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H, tb = blockIdx.x / H;
   const int64_t rows_total = (int64_t)Tq * H;
 
-  if (tid < 32) {
-    const int t = tb * 32 + tid;
+  if (tid < TB) {
+    const int t = tb * TB + tid;
     int sb = 0;
     if (t < Tq) sb = (seq_lens[seq_of_token(cu, batch, t)] + chunk - 1) / chunk;
     sb_s[tid] = sb;
   }
   __syncthreads();
-  constexpr int kLsePerThread = kCombineMaxSplits * 32 / kCombThreads;
+  constexpr int kLseTot = kCombineMaxSplits * TB;   // (split, row) pairs
+  constexpr int kLsePerThread = (kLseTot + kCombThreads - 1) / kCombThreads;
   {
     float x[kLsePerThread];
 #pragma unroll
     for (int u = 0; u < kLsePerThread; ++u) {
-      const int k = tid + kCombThreads * u, sp = k >> 5, r = k & 31;
-      x[u] = (sp < S_max && sp < sb_s[r]) ? lse[sp * rows_total + (int64_t)(tb * 32 + r) * H + h]
-                                          : -INFINITY;
+      const int k = tid + kCombThreads * u, sp = k / TB, r = k % TB;
+      x[u] = (k < kLseTot && sp < S_max && sp < sb_s[r])
+                 ? lse[sp * rows_total + (int64_t)(tb * TB + r) * H + h]
+                 : -INFINITY;
     }
 #pragma unroll
     for (int u = 0; u < kLsePerThread; ++u) {
       const int k = tid + kCombThreads * u;
-      if ((k >> 5) < S_max) w_s[k >> 5][k & 31] = x[u];
+      if (k < kLseTot && k / TB < S_max) w_s[k / TB][k % TB] = x[u];
     }
   }
   __syncthreads();
-  if (tid < 32) {
+  if (tid < TB) {
     float m = -INFINITY;
     for (int sp = 0; sp < S_max; ++sp) m = fmaxf(m, w_s[sp][tid]);
     float sum = 0.f;
@@ -242,15 +249,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   __syncthreads();
 
   {
-    constexpr int kRows = 32 * (kDc / 4) / kCombThreads;   // rows per thread (8)
-    constexpr int kSp = 2;                                  // splits per round of loads
+    constexpr int kRows = TB * (kDc / 4) / kCombThreads;   // rows per thread (TB / 4)
+    constexpr int kSp = 16 / kRows;                        // splits per round of loads
     const int j = 4 * (tid & 127), r0 = tid >> 7;
     f32x4 acc[kRows];
     const float* src[kRows];
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
       acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int t = min(tb * 32 + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
+      const int t = min(tb * TB + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
       src[u] = opart + ((int64_t)t * H + h) * kDc + j;
     }
     // splits a row's sequence has (the rows of one thread are the same for
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
 
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   if (wave >= 4) return;
-  const int t = tb * 32 + l32;
+  const int t = tb * TB + l32;
   const bf16* wh = wuv + (int64_t)h * dv * kDc;
   for (int vb = wave; vb < dv / 32; vb += 4) {
     constexpr int NS = kDc / 16, kGrp = 8;
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
         for (int u = 0; u < kGrp; ++u) a[grp & 1][u] = load_fragment(wh, vb, (grp + 2) * kGrp + u, kDc, lane);
       }
     }
-    if (t < Tq) {
+    if (l32 < TB && t < Tq) {
       bf16* dst = out + ((int64_t)t * H + h) * dv + vb * 32 + 4 * g;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
@@ -416,11 +423,22 @@ void launch_out_proj(int elem, const void* olat, const void* wuv, void* out, int
 
 void launch_combine_out(const SplitPlan& plan, const float* opart, const float* lse,
                         const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
-                        int batch, int Tq, int H, int dv, hipStream_t st) {
-  const unsigned blocks = (unsigned)(((Tq + 31) / 32) * H);
-  combine_out_bf16_kernel<<<blocks, kCombThreads, 0, st>>>(opart, lse, cu_q, seq_lens, (const bf16*)wuv,
-                                                  (bf16*)out, batch, Tq, H, dv, plan.chunk,
-                                                  plan.S_max);
+                        int batch, int Tq, int H, int dv, int num_cus, hipStream_t st) {
+  // the largest token block that still gives every compute unit a workgroup
+  int TB = 32;
+  while (TB > 4 && (int64_t)((Tq + TB - 1) / TB) * H < num_cus) TB /= 2;
+  const unsigned blocks = (unsigned)(((Tq + TB - 1) / TB) * H);
+  switch (TB) {
+#define MLA_COMBINE_CASE(N)                                                                     \
+  case N:                                                                                       \
+    combine_out_bf16_kernel<N><<<blocks, kCombThreads, 0, st>>>(                                \
+        opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H, dv, plan.chunk, \
+        plan.S_max);                                                                            \
+    break;
+    MLA_COMBINE_CASE(32) MLA_COMBINE_CASE(16) MLA_COMBINE_CASE(8) MLA_COMBINE_CASE(4)
+#undef MLA_COMBINE_CASE
+    default: break;
+  }
 }
 
 }  // namespace mla
