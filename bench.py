@@ -32,10 +32,13 @@ METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
+    ("ab8f42d3d585f435", "dsv2_b32_ctx4096"): {"fetch_bytes": 155911856, "write_bytes": 36308669},
+    ("ab8f42d3d585f435", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606554667, "write_bytes": 16811206},
+    ("ab8f42d3d585f435", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210448614, "write_bytes": 73067174},
 }
 
 
-ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip", "splitkv_x8p.hip")
+ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip")
 
 
 def splitkv_source_id():

@@ -2,7 +2,6 @@
 // buffer carving, the split plan, and kernel launches.  No device memory is
 // allocated here; every buffer comes from the caller.
 #include <math.h>
-#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -99,12 +98,9 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
   const int H = L->cfg.num_attention_heads;
   const int rows = max_q_len * H;
   if (L->elem == 2) {
-    // more than 32 rows: 64-row workgroups (the eight-wave kernel unless
-    // MLA_SPLITKV_KERNEL=x8p selects the pipelined one); else one 32-row block
+    // more than 32 rows: 64-row workgroups of eight waves; else one 32-row block
     if (rows > 32) {
-      const char* k = getenv("MLA_SPLITKV_KERNEL");
       p->NB = 8;
-      if (k && strcmp(k, "x8p") == 0) p->NB = 9;
       p->RQ = (rows + 63) / 64;
     } else {
       p->NB = 1;

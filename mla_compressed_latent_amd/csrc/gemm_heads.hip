@@ -37,20 +37,20 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float 
 
 // q_lat^T block = W_uk_h^T (32 latent rows x d_nope) . q_nope^T (d_nope x 32
 // tokens): the folded weight is the A operand, streamed as contiguous
-// fragments; the 32 query rows are the B operand.  One wave per (head, 128
-// latent columns, up to kAbsorbTokBlocks token blocks): its weight fragments
-// stay in registers while the token blocks stream past, so W_uk is read
-// about once per step however many query tokens there are.  The stored score operand
-// (q_lat and the rotated rope part) is pre-multiplied by qscale = softmax
-// scale * log2(e), so the attention kernel's scores come out in log2 units.  One wave per (32-token
-// block, head, kAbsorbJB column blocks); each lane stores 4 consecutive
-// latent values of one token.
+// fragments; the 32 query rows are the B operand.  One wave per (head, JB
+// blocks of 32 latent columns, up to kAbsorbTokBlocks token blocks): its
+// weight fragments stay in registers while the token blocks stream past, so
+// W_uk is read about once per step however many query tokens there are.
+// Each lane stores 4 consecutive latent values of one token.  The stored score
+// operand (q_lat and the rotated rope part) is pre-multiplied by qscale =
+// softmax scale * log2(e), so the attention kernel's scores come out in log2
+// units.
 //
 // Workgroups past the GEMM blocks rotate the rope part of the queries: one
 // per (sequence, block of kRopeTok of its query tokens, block of kRopeHeads
 // heads), so each angle is computed once and applied to every head of the
 // block.  Lane l handles pair l % 32 (d_rope = 64) for heads of parity l / 32.
-template <int NS>   // d_nope / 16
+template <int NS, int JB>   // d_nope / 16, 32-column blocks per wave (held in registers)
 __global__ __launch_bounds__(64) void absorb_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
@@ -87,7 +87,6 @@ __global__ __launch_bounds__(64) void absorb_bf16_kernel(
     }
     return;
   }
-  constexpr int JB = NS <= 8 ? 4 : 2;   // 32-column blocks per wave, held in registers
   const int JG = dc / 32 / JB;
   const int ntb = (Tq + 31) / 32;
   const int TBW = min(ntb, kAbsorbTokBlocks);   // token blocks per wave
@@ -208,6 +207,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H, tb = blockIdx.x / H;
   const int64_t rows_total = (int64_t)Tq * H;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+
+  // W_uv fragments of the first value-column block of waves 0..3, loaded
+  // first so that their latency hides under the combine
+  constexpr int kGrp = 8;
+  const bf16* wh = wuv + (int64_t)h * dv * kDc;
+  bf16x8 a[2][kGrp];
+  if (wave < 4 && wave < dv / 32) {
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) {
+      a[0][u] = load_fragment(wh, wave, u, kDc, lane);
+      a[1][u] = load_fragment(wh, wave, kGrp + u, kDc, lane);
+    }
+  }
 
   if (tid < TB) {
     const int t = tb * TB + tid;
@@ -296,18 +309,17 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   }
   __syncthreads();
 
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   if (wave >= 4) return;
   const int t = tb * TB + l32;
-  const bf16* wh = wuv + (int64_t)h * dv * kDc;
   for (int vb = wave; vb < dv / 32; vb += 4) {
-    constexpr int NS = kDc / 16, kGrp = 8;
+    constexpr int NS = kDc / 16;
     f32x16 acc = zero_f32x16();
-    bf16x8 a[2][kGrp];
+    if (vb != wave) {
 #pragma unroll
-    for (int u = 0; u < kGrp; ++u) {
-      a[0][u] = load_fragment(wh, vb, u, kDc, lane);
-      a[1][u] = load_fragment(wh, vb, kGrp + u, kDc, lane);
+      for (int u = 0; u < kGrp; ++u) {
+        a[0][u] = load_fragment(wh, vb, u, kDc, lane);
+        a[1][u] = load_fragment(wh, vb, kGrp + u, kDc, lane);
+      }
     }
 #pragma unroll
     for (int grp = 0; grp < NS / kGrp; ++grp) {
@@ -383,20 +395,22 @@ void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const i
   if (elem == 2) {
     const int ntb = (Tq + 31) / 32;
     const int tbw = ntb < kAbsorbTokBlocks ? ntb : kAbsorbTokBlocks;
+    // weight blocks per wave: 4 (2 when d_nope > 128) amortise the weight
+    // registers over many token blocks
     const int jb = dn / 16 <= 8 ? 4 : 2;
     const int gemm_blocks = ((ntb + tbw - 1) / tbw) * H * (dc / 32 / jb);
     const int TC = (max_q_len + kRopeTok - 1) / kRopeTok;
     const int HG = (H + kRopeHeads - 1) / kRopeHeads;
     const unsigned blocks = (unsigned)(gemm_blocks + batch * TC * HG);
-    switch (dn / 16) {
-#define MLA_ABSORB_CASE(NS)                                                                   \
-  case NS:                                                                                    \
-    absorb_bf16_kernel<NS><<<blocks, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk,          \
-                                                  (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, \
-                                                  gemm_blocks, TC, freq, qscale);             \
+    switch (dn / 16 * 8 + jb) {
+#define MLA_ABSORB_CASE(NS, JB)                                                                    \
+  case NS * 8 + JB:                                                                                \
+    absorb_bf16_kernel<NS, JB><<<blocks, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk,           \
+                                                      (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, \
+                                                      gemm_blocks, TC, freq, qscale);             \
     break;
-      MLA_ABSORB_CASE(2) MLA_ABSORB_CASE(4) MLA_ABSORB_CASE(6) MLA_ABSORB_CASE(8)
-      MLA_ABSORB_CASE(10) MLA_ABSORB_CASE(12) MLA_ABSORB_CASE(14) MLA_ABSORB_CASE(16)
+      MLA_ABSORB_CASE(2, 4) MLA_ABSORB_CASE(4, 4) MLA_ABSORB_CASE(6, 4) MLA_ABSORB_CASE(8, 4)
+      MLA_ABSORB_CASE(10, 2) MLA_ABSORB_CASE(12, 2) MLA_ABSORB_CASE(14, 2) MLA_ABSORB_CASE(16, 2)
 #undef MLA_ABSORB_CASE
       default: break;   // excluded by the config check
     }

@@ -700,10 +700,6 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
   if (elem == 2) {
     const int nblocks = batch * plan.S_max * plan.RQ;
     switch (plan.NB) {
-      case 9:
-        launch_splitkv_x8p(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                           page_size, opart, lse, st);
-        break;
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
                           page_size, opart, lse, st);

@@ -32,15 +32,12 @@ def _sampled(name):
     return wl, [0, wl.batch - 1], [0, H // 2 + 5, H - 1]
 
 
-@pytest.mark.parametrize("kernel", ["x8", "x8p"])
 @pytest.mark.parametrize("name", ["dsv2_b32_ctx4096", "llama2_7b_mla_b64_ctx8192", "dsv2_b8_ctx131072",
                                   "dsv2_ragged_paged_256"])
-def test_full_size_sampled(name, kernel, monkeypatch):
-    # every 64-row split-KV kernel; the library reads MLA_SPLITKV_KERNEL per call
-    monkeypatch.setenv("MLA_SPLITKV_KERNEL", kernel)
+def test_full_size_sampled(name):
     wl, seqs, heads = _sampled(name)
     t0 = time.time()
-    print(f"\n[full] {name} kernel={kernel}: B={wl.batch}, max context {int(wl.seq_lens().max())}, building the cache",
+    print(f"\n[full] {name}: B={wl.batch}, max context {int(wl.seq_lens().max())}, building the cache",
           flush=True)
     case = GpuCase(wl, fill_sentinel=False)
     print(f"[full] {name}: cache built in {time.time() - t0:.0f}s; append + decode", flush=True)

@@ -28,15 +28,6 @@ BF16_REL_MAX = 1e-2
 BF16_REL_RMS = 1e-2
 
 
-@pytest.fixture(autouse=True, params=["x8", "x8p"])
-def splitkv_waves(request, monkeypatch):
-    """Both 64-row split-KV kernels (eight-wave, pipelined eight-wave) run
-    every case; the library reads MLA_SPLITKV_KERNEL when it plans a call."""
-    monkeypatch.setenv("MLA_SPLITKV_KERNEL", request.param)
-    print(f"[parity] MLA_SPLITKV_KERNEL={request.param}", flush=True)
-    return request.param
-
-
 def _check(case: GpuCase, out: torch.Tensor, seqs=None, heads=None, tag=""):
     wl = case.wl
     got = out.float().cpu().numpy()
