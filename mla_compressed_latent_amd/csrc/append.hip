@@ -70,33 +70,38 @@ __global__ __launch_bounds__(64) void append_finish_kernel(
     const int32_t* __restrict__ prefix_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, T* __restrict__ cache, int page_size, int dc, int dr, float base,
     const RopeFreq freq) {
-  __shared__ CuStage cu_st;
-  const int32_t* cu = stage_cu(cu_st, cu_new, batch);
   const int t = blockIdx.x;
   const int D = dc + dr;
   const int p = blockIdx.y * 64 + threadIdx.x;
+  const int n = 2 * p;
+  const int64_t stride = (int64_t)T_new * D;
+  // the k-split partials first (they depend on nothing), so that their
+  // latency overlaps the chain of lookups that finds the token's page slot;
+  // up to 32 splits in flight, summed in split order
+  const float* src = part + (int64_t)t * D + min(n, D - 2);
+  float2 v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    v[j] = j < ksplits ? *reinterpret_cast<const float2*>(src + j * stride) : float2{0.f, 0.f};
+  __shared__ CuStage cu_st;
+  const int32_t* cu = stage_cu(cu_st, cu_new, batch);
   if (p >= D / 2) return;
   const int b = seq_of_token(cu, batch, t);
   const int pos = prefix_lens[b] + (t - cu[b]);
   const int page = page_table[(int64_t)b * max_pages + pos / page_size];
   T* dst = cache + ((int64_t)page * page_size + pos % page_size) * D;
-  const int n = 2 * p;
-  const int64_t stride = (int64_t)T_new * D;
-  const float2* src = reinterpret_cast<const float2*>(part + (int64_t)t * D + n);
   float u0 = 0.f, u1 = 0.f;
-  int ks = 0;
-  for (; ks + 4 <= ksplits; ks += 4) {
-    float2 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float2*>(
-        reinterpret_cast<const float*>(src) + (ks + j) * stride);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { u0 += v[j].x; u1 += v[j].y; }
+  for (int j = 0; j < 32; ++j) {
+    if (j < ksplits) {
+      u0 += v[j].x;
+      u1 += v[j].y;
+    }
   }
-  for (; ks < ksplits; ++ks) {
-    const float2 v = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(src) + ks * stride);
-    u0 += v.x;
-    u1 += v.y;
+  for (int ks = 32; ks < ksplits; ++ks) {
+    const float2 w = *reinterpret_cast<const float2*>(src + ks * stride);
+    u0 += w.x;
+    u1 += w.y;
   }
   if (n >= dc) {
     float c, s;

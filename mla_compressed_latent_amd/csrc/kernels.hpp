@@ -44,7 +44,7 @@ struct SplitPlan {
   int chunk;    // tokens per work item (multiple of 64)
   int S_max;    // splits of the longest sequence
   int RQ;       // row groups per sequence (bf16 path)
-  int NB;       // bf16 path: 32-row blocks per workgroup (1, 2, 4), or 8: 64-row eight-wave kernel
+  int NB;       // bf16 path: 1 = one 32-row block per workgroup, 8 = 64-row eight-wave kernel
 };
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
@@ -61,7 +61,6 @@ void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cach
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, float* opart,
                        float* lse, hipStream_t st);
-// 64 query rows per workgroup, sixteen waves (bf16 layers, plan.NB == 16).
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

@@ -12,21 +12,21 @@
 // row (online softmax), and leaves a normalised partial O and its log-sum-exp;
 // the combine kernel merges the splits.
 //
-// bf16 path (d_c = 512, d_rope = 64), one workgroup of 4 waves per (sequence,
-// split, block of NB * 32 rows):
+// bf16 path, at most 32 rows per sequence (d_c = 512, d_rope = 64; more rows
+// go to the eight-wave kernel of splitkv_x8.hip), one workgroup of 4 waves per
+// (sequence, split):
 //   * 32-token tiles of cached rows are copied HBM -> LDS by the LDS-DMA path
 //     (global_load_lds, 16 bytes per lane, every wave copies 8 rows), three
 //     tiles in flight; 16-byte chunks are swizzled per row (swz) so that both
 //     operand reads below are free of bank conflicts;
-//   * score waves (0 .. NB-1) keep their 32 rows of the score operand (32 x
-//     576 bf16) in registers and compute S^T = tile . A^T on the 32x32x16 bf16
+//   * the score wave (0) keeps the 32 rows of the score operand (32 x 576
+//     bf16) in registers and computes S^T = tile . A^T on the 32x32x16 bf16
 //     matrix core (36 MFMAs per tile), then the online softmax in the
-//     accumulator layout (one row per lane pair), and hand the bf16
+//     accumulator layout (one row per lane pair), and hands the bf16
 //     probabilities to LDS;
-//   * value waves (2, 3) each accumulate O^T for all rows over half of d_c
-//     (256 columns, 256 accumulator registers at NB = 2), reading the value
-//     operand straight out of the token-major tile with the transposing LDS
-//     load (ds_read_b64_tr_b16);
+//   * value waves (2, 3) each accumulate O^T for the 32 rows over half of d_c
+//     (256 columns), reading the value operand straight out of the
+//     token-major tile with the transposing LDS load (ds_read_b64_tr_b16);
 //   * the score waves work one tile ahead of the value waves, so the two kinds
 //     of matrix work overlap; one barrier per tile.
 #include "attn_tile.hpp"
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
     float* __restrict__ opart, float* __restrict__ lse) {
-  static_assert(NB == 1 || NB == 2, "row blocks per workgroup");
+  static_assert(NB == 1, "one 32-row block per workgroup");
   constexpr int kDbPerPv = kDC / 32 / 2;       // 32-wide value blocks per value wave (8)
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kNBuf][kTileTok * kD];
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NB][2][64];
@@ -310,257 +310,6 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   }
 }
 
-// 128 rows per workgroup (H*q_len >= 128): every wave scores its own 32 rows
-// and accumulates 128 value columns for all four row blocks, so each cached
-// tile crosses the memory fabric once.  Score operand: d_c part in registers
-// (128 VGPRs), rope part in LDS.  Value accumulators: 4 x 4 blocks = all 256
-// AGPRs of the wave.
-__global__ __launch_bounds__(256, 1) void splitkv_bf16_rows128_kernel(
-    const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
-    int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
-    float* __restrict__ opart, float* __restrict__ lse) {
-  constexpr int NB = 4, kNBuf4 = 3;
-  constexpr int kQReg = kDC / 16;                // 32 k-steps of the score operand in registers
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[kNBuf4][kTileTok * kD];
-  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[NB][2][64];
-  __shared__ __attribute__((aligned(16))) bf16x8 qrope_s[NB][kDR / 16][64];
-  __shared__ float alpha_s[NB][32];
-  __shared__ float lrow_s[NB][32];
-  __shared__ int pages_s[kMaxChunkPages];
-
-  const int nblocks = batch * S_max * RQ;
-  const int logical = xcd_logical_block(blockIdx.x, nblocks);
-  const int rq = logical % RQ;
-  const int s = (logical / RQ) % S_max;
-  const int b = logical / (RQ * S_max);
-
-  const int q0 = cu_q[b];
-  const int Lq = cu_q[b + 1] - q0;
-  const int L = seq_lens[b];
-  const int R = Lq * H;
-  const int row_base = rq * NB * 32;
-  const int tok_begin = s * chunk;
-  if (row_base >= R || tok_begin >= L) return;
-  const int tok_end = min(tok_begin + chunk, L);
-  const int ntiles = (tok_end - tok_begin + kTileTok - 1) / kTileTok;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int64_t rows_total = (int64_t)Tq * H;
-
-  const int page0 = tok_begin / page_size;
-  const int npages = (tok_end - 1) / page_size - page0 + 1;
-  for (int i = threadIdx.x; i < npages; i += blockDim.x)
-    pages_s[i] = page_table[(int64_t)b * max_pages + page0 + i];
-
-  uint32_t dma_off[kDmaPerWave];
-#pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u) {
-    const int slot = (wave * kDmaPerWave + u) * 64 + lane;
-    const int t = slot / kChunks;
-    dma_off[u] = (uint32_t)(t * kChunks + ((slot % kChunks) ^ swz(t))) * 16u;
-  }
-  const uint32_t lds_tiles = lds_address(&tiles[0][0]);
-
-  // score rows of this wave
-  const int my_row = row_base + wave * 32 + l32;
-  const bool row_ok = my_row < R;
-  const int my_i = row_ok ? my_row / H : 0;
-  const int my_h = row_ok ? my_row % H : 0;
-  const int my_limit = row_ok ? (L - Lq + my_i) : -1;
-  bf16x8 qf[kQReg];
-  {
-    const bf16* qrow = abuf + ((int64_t)(q0 + my_i) * H + my_h) * kD + 8 * g;
-    const uint32_t keep = row_ok ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      u32x4 v = __builtin_bit_cast(u32x4, load_bf16x8(qrow + 16 * ks));
-      v &= keep;
-      if (ks < kQReg) qf[ks] = __builtin_bit_cast(bf16x8, v);
-      else qrope_s[wave][ks - kQReg][lane] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  __syncthreads();   // pages and rope operand staged
-
-  auto issue_tile = [&](int it) {
-    const int tok0 = tok_begin + it * kTileTok;
-    const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
-    const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
-    const uint32_t lds0 =
-        lds_tiles + (uint32_t)((it % kNBuf4) * kTileBytes + wave * kDmaPerWave * 1024);
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
-  };
-
-  uint32_t qk_base[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) qk_base[j] = (uint32_t)(l32 * kChunks + ((2 * j + g) ^ swz(l32))) * 16u;
-  // value operand (transposing read), this wave's dims [128 wave, 128 wave + 128)
-  uint32_t pv_base[2][2];
-  {
-    const int k = lane >> 4, sl = lane & 15, j = sl >> 2, q = sl & 3;
-#pragma unroll
-    for (int e1 = 0; e1 < 2; ++e1)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int t = 4 * g + j + 16 * ks;
-        const int c = 16 * wave + 4 * e1 + 2 * (k & 1) + (q >> 1);
-        pv_base[e1][ks] = (uint32_t)(t * kChunks + (c ^ swz(t))) * 16u + 8u * (q & 1);
-      }
-  }
-
-  f32x16 O[4][NB];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rb = 0; rb < NB; ++rb) O[db][rb] = zero_f32x16();
-  float m_run = -INFINITY, l_run = 0.f;
-
-  auto zero_tail = [&](int it) {
-    const int nvalid = tok_end - (tok_begin + it * kTileTok);
-    if (nvalid < kTileTok) {
-      u32x4* rows = reinterpret_cast<u32x4*>(&tiles[it % kNBuf4][0]) + nvalid * kChunks;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int i = threadIdx.x; i < (kTileTok - nvalid) * kChunks; i += blockDim.x) rows[i] = z;
-      __syncthreads();
-    }
-  };
-
-  for (int p = 0; p < kNBuf4 - 1; ++p)
-    if (p < ntiles) issue_tile(p);
-
-  for (int it = 0; it < ntiles; ++it) {
-    wait_tiles_ahead(min(kNBuf4 - 2, ntiles - 1 - it));
-    __syncthreads();                         // tile it landed everywhere; tile it-1 retired
-    if (it + kNBuf4 - 1 < ntiles) issue_tile(it + kNBuf4 - 1);
-    zero_tail(it);
-    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf4][0]);
-    const int tok0 = tok_begin + it * kTileTok;
-
-    // ---- scores S^T = tile . A^T for this wave's 32 rows
-    {
-      constexpr int kGroups = kD / 64;
-      constexpr int kRing = 2;
-      bf16x8 ring[kRing][4];
-#pragma unroll
-      for (int grp = 0; grp < kRing; ++grp)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ring[grp][j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * grp);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 acc;
-#pragma unroll
-      for (int grp = 0; grp < kGroups; ++grp) {
-        bf16x8 (&a)[4] = ring[grp % kRing];
-        bf16x8 qv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          qv[j] = (4 * grp + j < kQReg) ? qf[(4 * grp + j) % kQReg] : qrope_s[wave][j][lane];
-        if (grp == 0)
-          qk_mfma4_first(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
-        else if (grp == kGroups - 1)
-          qk_mfma4_last(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
-        else
-          qk_mfma4(acc, a[0], qv[0], a[1], qv[1], a[2], qv[2], a[3], qv[3]);
-        if (grp + kRing < kGroups) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            a[j] = *reinterpret_cast<const bf16x8*>(tileb + qk_base[j] + 128 * (grp + kRing));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      bf16x8 pf0, pf1;
-      const bool masked = tok0 + kTileTok - 1 > L - Lq;
-      const float alpha = softmax_tile(acc, masked, tok0, my_limit, scale_log2e, m_run, l_run, pf0, pf1);
-      pbuf[wave][0][lane] = pf0;
-      pbuf[wave][1][lane] = pf1;
-      if (g == 0) alpha_s[wave][l32] = alpha;
-    }
-    __syncthreads();
-
-    // ---- values: O^T += tile^T P^T over this wave's 128 dims, all 4 row blocks
-    {
-      {  // rare: a row's running max grew past the threshold -> rescale its O
-        float al[NB];
-        bool any = false;
-#pragma unroll
-        for (int rb = 0; rb < NB; ++rb) {
-          al[rb] = alpha_s[rb][l32];
-          any |= __any(al[rb] != 1.f);
-        }
-        if (any) {
-          pv_drain<NB, 4>(O);
-#pragma unroll
-          for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              O[db][rb] *= al[rb];
-              asm volatile("" : "+a"(O[db][rb]));
-            }
-        }
-      }
-      constexpr int kSteps = 8, kRing = 4;
-      auto frag_addr = [&](int st, int hl) {
-        const int ks = st / 4, db = st % 4;
-        return tileb + pv_base[(db & 1) ^ hl][ks] + kChunks * 16 * 8 * hl + 128 * (db >> 1);
-      };
-      v4bf16 ring[kRing][2];
-#pragma unroll
-      for (int st = 0; st < kRing; ++st) {
-        ring[st][0] = ds_read_tr16(frag_addr(st, 0));
-        ring[st][1] = ds_read_tr16(frag_addr(st, 1));
-      }
-      bf16x8 pb[NB];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const int ks = st / 4, db = st % 4;
-        if (db == 0) {
-#pragma unroll
-          for (int rb = 0; rb < NB; ++rb) pb[rb] = pbuf[rb][ks][lane];
-        }
-        v4bf16 (&f)[2] = ring[st % kRing];
-        const bf16x8 a = __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        pv_mfma<NB>(O[db], a, pb);
-        if (st + kRing < kSteps) {
-          f[0] = ds_read_tr16(frag_addr(st + kRing, 0));
-          f[1] = ds_read_tr16(frag_addr(st + kRing, 1));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  pv_drain<NB, 4>(O);
-
-  // ---- epilogue: row statistics, then normalised partials
-  if (g == 0) lrow_s[wave][l32] = l_run;
-  if (g == 0 && my_row < R) {
-    const int64_t rowg = (int64_t)(q0 + my_i) * H + my_h;
-    lse[(int64_t)s * rows_total + rowg] = (l_run > 0.f) ? m_run + log2f(l_run) : -INFINITY;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb) {
-    const int row = row_base + rb * 32 + l32;
-    if (row >= R) continue;
-    const float lr = lrow_s[rb][l32];
-    const float inv = lr > 0.f ? 1.f / lr : 0.f;
-    const int64_t rowg = (int64_t)(q0 + row / H) * H + row % H;
-    float* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + wave * 128;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = O[db][rb][4 * q4 + e] * inv;
-        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * q4 + 4 * g) = v;
-      }
-  }
-}
-
 // ---------------------------------------------------------------- fp32 path
 // One workgroup per (query row, split); 64-token tiles; VALU dot products.
 constexpr int kF32Tile = 64;
@@ -703,16 +452,6 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
                           page_size, opart, lse, st);
-        break;
-      case 4:
-        splitkv_bf16_rows128_kernel<<<nblocks, 256, 0, st>>>(
-            (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-            page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
-        break;
-      case 2:
-        splitkv_bf16_kernel<2><<<nblocks, 256, 0, st>>>(
-            (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-            page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
         break;
       default:
         splitkv_bf16_kernel<1><<<nblocks, 256, 0, st>>>(
