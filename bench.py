@@ -32,9 +32,9 @@ METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("ab8f42d3d585f435", "dsv2_b32_ctx4096"): {"fetch_bytes": 155911856, "write_bytes": 36308669},
-    ("ab8f42d3d585f435", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606554667, "write_bytes": 16811206},
-    ("ab8f42d3d585f435", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210448614, "write_bytes": 73067174},
+    ("ca6764d795ac493c", "dsv2_b32_ctx4096"): {"fetch_bytes": 155910612, "write_bytes": 35831633},
+    ("ca6764d795ac493c", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606557504, "write_bytes": 16811723},
+    ("ca6764d795ac493c", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210457128, "write_bytes": 72269077},
 }
 
 
@@ -193,6 +193,7 @@ def cpu_baseline(wl, budget_s):
     done_q = 0
     elapsed = 0.0
     seqs = 0
+    flops = 0.0
     with threadpool_limits(limits=cores):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         for b in range(wl.batch):
@@ -209,12 +210,28 @@ def cpu_baseline(wl, budget_s):
             elapsed += time.perf_counter() - t0
             done_q += q.shape[0]
             seqs += 1
+            # float64 work of that sample: latent rows of the new tokens, per-head
+            # K and V materialised over the whole sequence, scores and sums
+            L, lq = cache.shape[0], q.shape[0]
+            flops += 2.0 * lq * s.d_model * (s.d_c + s.d_rope)
+            flops += 2.0 * s.H * L * s.d_c * (s.d_nope + s.d_v)
+            flops += 2.0 * lq * s.H * L * (s.d_nope + s.d_rope + s.d_v)
             if elapsed >= budget_s:
                 break
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    blas = sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                   for i in threadpool_info() if i.get("user_api") == "blas"})
     return {
         "value": done_q / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": f"{seqs} of {wl.batch} sequences ({done_q} query tokens, all {s.H} heads), "
                   f"append + unabsorbed float64 attention, {elapsed:.1f}s",
+        "seconds": elapsed, "fp64_gflop": flops / 1e9, "fp64_gflops_per_s": flops / elapsed / 1e9,
+        "cpu_model": cpu_model, "host_cpus": os.cpu_count(), "blas": blas,
     }
 
 
@@ -254,6 +271,7 @@ def main():
     torch.cuda.synchronize()
     eager_ms = t_e0.elapsed_time(t_e1) / KP
     phase = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / KP for j in range(4)]
+    attend_each = sorted(e[2].elapsed_time(e[3]) for e in evs)
 
     # The timed steps run as HIP graphs, as a serving loop runs a decode
     # forward: the R rotated copies of {cache, folded weights} are R distinct
@@ -282,15 +300,40 @@ def main():
         g_all.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K // R + 1)]
     start.record()
+    marks[0].record()
     for i in range(K // R):
         g_all.replay()
+        marks[i + 1].record()
     for g in singles:
         g.replay()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) / R for i in range(K // R))
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))] if v else None
+
+    # The same steps with every step on copy 0: the 256 MB last-level cache
+    # may then serve part of the cache from the previous step ("MALL-warm").
+    with torch.cuda.stream(cap):
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=cap):
+            for r in range(R):
+                run_step(st, 0)
+    torch.cuda.current_stream().wait_stream(cap)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    for i in range(max(1, K // R)):
+        g_warm.replay()
+    w1.record()
+    torch.cuda.synchronize()
+    warm_ms_step = w0.elapsed_time(w1) / (max(1, K // R) * R)
     s = st["s"]
     latent_bytes = int(st["seq_lens_np"].astype("int64").sum()) * s.row_width * (2 if s.dtype == "bf16" else 4)
     attend_s = phase[2] * 1e-3
@@ -322,7 +365,11 @@ def main():
         "latent_cache_GBps": achieved,
         "latent_cache_frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
         "timing": "HIP graph replay of whole steps (append + decode); one graph holds one step on each of the R rotated layer copies",
+        "ms_per_step_p10_p50_p90": [pct(per_step, 0.1), pct(per_step, 0.5), pct(per_step, 0.9)],
+        "mall_warm_ms_per_step": warm_ms_step,
+        "end_to_end_latent_GBps": latent_bytes / (ms_step * 1e-3) / 1e9,
         "eager_ms_per_step": eager_ms,
+        "attend_us_p10_p50_p90": [pct(attend_each, q) * 1e3 for q in (0.1, 0.5, 0.9)],
         "phase_us": {"append": phase[0] * 1e3, "absorb": phase[1] * 1e3, "attend": phase[2] * 1e3,
                      "combine_and_output": phase[3] * 1e3},
         "roofline": {
@@ -340,6 +387,10 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    props = torch.cuda.get_device_properties(0)
+    res["hardware"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                       "compute_units": props.multi_processor_count,
+                       "memory_GB": round(props.total_memory / 1e9, 1)}
     print(json.dumps(res), flush=True)
 
 
