@@ -9,8 +9,12 @@ Inputs are synthetic and seeded, already resident in HBM when timing starts.
 R copies of {cache, folded weights} (>= 1 GiB together) are used in turn so
 that the 256 MB last-level cache cannot serve a step from the previous one.
 
+Workloads of kind "extend" (long new chunks: chunked extend, prefill) time
+append + mla_extend instead, by the form --path names (default: the
+library's choice) and report matrix-core throughput.
+
 Prints one JSON line.  Usage:
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path P]
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode tokens/s and achieved latent-cache HBM GB/s (% of peak), 1 GPU"
+EXTEND_METRIC = "MLA chunked-extend / prefill query tokens/s and matrix-core TFLOP/s, 1 GPU"
 
 # HBM bytes per split-KV launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled
 # by the same counters on a 256 MiB device copy (x2.000 and x1.000), keyed by
@@ -64,6 +69,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("auto", "absorbed", "expanded"), default="auto",
+                    help="form of mla_extend for extend workloads")
     return ap.parse_args()
 
 
@@ -71,7 +78,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_state(wl, kv_chunk, rotate):
+def build_state(wl, kv_chunk, rotate, path="auto"):
     import numpy as np
     import torch
 
@@ -150,16 +157,39 @@ def build_state(wl, kv_chunk, rotate):
     )
     st["chunk"] = mla.mla_decode_kv_chunk(layer0, B, st["max_q_len"], st["max_seq_len"], kv_chunk)
     st["aws"] = torch.empty(max(1, mla.mla_append_workspace_bytes(layer0, Tq)), dtype=torch.uint8, device=dev)
-    st["dws"] = torch.empty(max(1, mla.mla_decode_workspace_bytes(layer0, B, Tq, st["max_q_len"],
-                                                                  st["max_seq_len"], kv_chunk)),
-                            dtype=torch.uint8, device=dev)
+    st["extend"] = wl.kind == "extend"
+    if st["extend"]:
+        chosen = mla.mla_extend_choose_path(cfg, B, Tq, st["max_q_len"], st["max_seq_len"])
+        st["auto_path"] = chosen
+        st["path"] = {"auto": chosen, "absorbed": mla.MLA_EXTEND_ABSORBED,
+                      "expanded": mla.MLA_EXTEND_EXPANDED}[path]
+        n = max(mla.mla_extend_workspace_bytes(layer0, B, Tq, st["max_q_len"], st["max_seq_len"], p)
+                for p in (mla.MLA_EXTEND_ABSORBED, mla.MLA_EXTEND_EXPANDED))
+        st["dws"] = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
+    else:
+        st["dws"] = torch.empty(max(1, mla.mla_decode_workspace_bytes(layer0, B, Tq, st["max_q_len"],
+                                                                      st["max_seq_len"], kv_chunk)),
+                                dtype=torch.uint8, device=dev)
     return st
 
 
-def run_step(st, i, ev=None):
+def run_step(st, i, ev=None, path=None):
     mla = st["mla"]
     r = i % st["R"]
     layer, cache = st["layers"][r], st["caches"][r]
+    if st["extend"]:
+        if ev is not None:
+            ev[0].record()
+        mla.mla_append_latent(layer, st["x_new"], st["cu_q"], st["prefix"], st["table"], cache,
+                              workspace=st["aws"])
+        if ev is not None:
+            ev[1].record()
+        mla.mla_extend(layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["out"],
+                       st["max_q_len"], st["max_seq_len"], path=st["path"] if path is None else path,
+                       workspace=st["dws"])
+        if ev is not None:
+            ev[2].record()
+        return
     args = (layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["out"], st["max_q_len"],
             st["max_seq_len"], st["kv_chunk"], st["dws"])
     if ev is not None:
@@ -176,6 +206,24 @@ def run_step(st, i, ev=None):
     mla.mla_decode_phases(*args, phases=mla.MLA_PHASE_OUTPUT)
     if ev is not None:
         ev[4].record()
+
+
+def extend_flops(wl, seq_lens, expanded):
+    """Matrix-core flops of one mla_extend call: causal key counts per query;
+    the expanded form builds K and V for every cached token of every head and
+    scores at width d_nope + d_rope + d_v, the absorbed form folds each query
+    in and out of latent space and scores at width 2 d_c + d_rope."""
+    s = wl.shape
+    keys = 0.0
+    for L, lq in zip(seq_lens, wl.q_lens()):
+        L, lq = int(L), int(lq)
+        keys += lq * (L - lq) + lq * (lq + 1) / 2.0
+    Tq = float(wl.q_lens().sum())
+    if expanded:
+        expand = 2.0 * s.H * s.d_c * (s.d_nope + s.d_v) * float(sum(int(L) for L in seq_lens))
+        return expand, 2.0 * s.H * (s.d_nope + s.d_rope + s.d_v) * keys
+    fold = 2.0 * s.H * s.d_c * (s.d_nope + s.d_v) * Tq
+    return fold, 2.0 * s.H * (2 * s.d_c + s.d_rope) * keys
 
 
 def cpu_baseline(wl, budget_s):
@@ -250,7 +298,9 @@ def main():
     wl = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     log(f"workload {wl.name}: {wl.description}")
-    st = build_state(wl, args.kv_chunk, args.rotate)
+    st = build_state(wl, args.kv_chunk, args.rotate, args.path)
+    if st["extend"]:
+        return main_extend(args, wl, st)
     log(f"kv_chunk {st['chunk']}, {st['R']} rotated copies of cache ({st['cache_bytes'] / 1e6:.1f} MB) "
         f"+ folded weights ({st['folded_bytes'] / 1e6:.1f} MB)")
 
@@ -384,6 +434,106 @@ def main():
     }
     log(f"{ms_step * 1e3:.1f} us/step (graph), {eager_ms * 1e3:.1f} us/step eager, attend "
         f"{phase[2] * 1e3:.1f} us -> {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak)")
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the host ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    props = torch.cuda.get_device_properties(0)
+    res["hardware"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                       "compute_units": props.multi_processor_count,
+                       "memory_GB": round(props.total_memory / 1e9, 1)}
+    print(json.dumps(res), flush=True)
+
+
+def main_extend(args, wl, st):
+    """Chunked extend / prefill: HIP-graph replay of append + mla_extend."""
+    import torch
+
+    mla = st["mla"]
+    s = st["s"]
+    names = {mla.MLA_EXTEND_ABSORBED: "absorbed", mla.MLA_EXTEND_EXPANDED: "expanded"}
+    for i in range(args.warmup):
+        run_step(st, i)
+    torch.cuda.synchronize()
+    K = args.steps
+    # eager per-phase times of both forms (the choice's evidence)
+    path_ms = {}
+    phase = None
+    for p in (mla.MLA_EXTEND_ABSORBED, mla.MLA_EXTEND_EXPANDED):
+        run_step(st, 0, path=p)
+        n = min(K, 5)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            run_step(st, i, evs[i], path=p)
+        torch.cuda.synchronize()
+        ph = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n for j in range(2)]
+        path_ms[names[p]] = ph[1]
+        if p == st["path"]:
+            phase = ph
+    R = st["R"]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all, stream=cap):
+            for r in range(R):
+                run_step(st, r)
+        singles = []
+        for r in range(K % R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                run_step(st, r)
+            singles.append(g)
+    torch.cuda.current_stream().wait_stream(cap)
+    g_all.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K // R):
+        g_all.replay()
+    for g in singles:
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    expanded = st["path"] == mla.MLA_EXTEND_EXPANDED
+    f_side, f_attn = extend_flops(wl, st["seq_lens_np"], expanded)
+    ext_s = phase[1] * 1e-3
+    tflops = (f_side + f_attn) / ext_s / 1e12
+    res = {
+        "metric": EXTEND_METRIC,
+        "value": st["Tq"] * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded Gaussian hidden states and weights)",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "query_tokens": st["Tq"],
+            "max_context": st["max_seq_len"], "heads": s.H, "kv_lora_rank": s.d_c,
+            "path": names[st["path"]], "auto_path": names[st["auto_path"]], "rotated_copies": R,
+        },
+        "timing": "HIP graph replay of whole steps (append + mla_extend); one graph holds one step on "
+                  "each of the R rotated layer copies",
+        "phase_ms": {"append": phase[0], "extend": phase[1]},
+        "extend_ms_by_path": path_ms,
+        "roofline": {
+            "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": f"mla_extend ({names[st['path']]}: both of its kernels, HIP events around the call)",
+            "algorithmic_flops_per_launch": f_side + f_attn,
+            "flops_split": {"expand_or_fold": f_side, "attention": f_attn},
+        },
+    }
+    log(f"{ms_step:.3f} ms/step (graph); extend {phase[1]:.3f} ms by the {names[st['path']]} form "
+        f"-> {tflops:.0f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of bf16 peak); "
+        f"by form: {path_ms}")
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

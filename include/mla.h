@@ -201,6 +201,61 @@ mla_status mla_decode_phases(const mla_layer* layer, const void* q, const int32_
                              void* workspace, size_t workspace_bytes, void* hip_stream,
                              uint32_t phases);
 
+/* Prefill and chunked extend: many new query tokens per sequence over the
+ * same paged cache ("Multi-head Latent Attention and KV Cache Compression",
+ * sections "The absorption trick and decoupled RoPE" and "What separates
+ * expressiveness at an equal cache budget": absorption can raise prefill
+ * compute; "Multi-head Latent Attention: the KV cache, compressed", section
+ * "Absorption: the part that makes it free": at real d_c / head-width ratios
+ * the absorbed form is not always fewer multiply-accumulates).
+ *
+ * Two ways to compute the same result:
+ *   MLA_EXTEND_ABSORBED  exactly mla_decode with kv_chunk 0;
+ *   MLA_EXTEND_EXPANDED  each head's content keys c W_uk_h and values
+ *                        c W_uv_h are built once per cached token into the
+ *                        workspace, then causal flash attention runs at width
+ *                        d_nope + d_rope (scores) and d_v (values).  bf16
+ *                        layers with qk_nope_head_dim and v_head_dim each 64
+ *                        or 128;
+ *   MLA_EXTEND_AUTO      the form with less matrix-core work for these
+ *                        bounds (see mla_extend_choose_path). */
+typedef enum {
+  MLA_EXTEND_AUTO = 0,
+  MLA_EXTEND_ABSORBED = 1,
+  MLA_EXTEND_EXPANDED = 2
+} mla_extend_path;
+
+/* The form MLA_EXTEND_AUTO takes for these host bounds: MLA_EXTEND_EXPANDED
+ * when it is available for cfg and its estimated matrix-core work,
+ *   batch*max_seq_len*H*2*d_c*(d_nope+d_v) + total_q*H*2*(d_nope+d_rope+d_v)*K,
+ * is below the absorbed form's,
+ *   total_q*H*(2*d_c*(d_nope+d_v) + 2*(2*d_c+d_rope)*K),
+ * with K = max_seq_len - max_q_len/2 keys per query; else
+ * MLA_EXTEND_ABSORBED.  Host-only (no device call).  -1 on invalid
+ * arguments (same bounds as mla_extend). */
+int32_t mla_extend_choose_path(const mla_config* cfg, int32_t batch, int32_t total_q,
+                               int32_t max_q_len, int32_t max_seq_len);
+
+/* Workspace mla_extend needs for these bounds and path (AUTO resolved as
+ * above).  Expanded: batch * H * lmax * (d_nope + d_v) * 2 bytes (plus
+ * alignment), lmax = max_seq_len rounded up to a multiple of 128.  0 on
+ * invalid arguments or when the path is unavailable for the layer. */
+size_t mla_extend_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
+                                  int32_t max_q_len, int32_t max_seq_len, int32_t path);
+
+/* Attention of every query over its sequence's cache, with the arguments,
+ * layout and result of mla_decode (queries before rotation, append first,
+ * query i of b at position seq_lens[b] - q_len_b + i, causal).  `path` is an
+ * mla_extend_path.  The workspace (>= mla_extend_workspace_bytes for the same
+ * path, 256-byte aligned) is scratch for this call only.
+ * Errors: INVALID_ARG, UNSUPPORTED (EXPANDED on a layer it does not cover),
+ * INSUFFICIENT_WORKSPACE, HIP. */
+mla_status mla_extend(const mla_layer* layer, const void* q, const int32_t* cu_q,
+                      const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                      int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                      int32_t path, const void* cache, int64_t num_pages, void* out,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 

@@ -20,7 +20,8 @@ __all__ = [
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
     "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
     "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
-    "MLA_PHASE_ALL",
+    "MLA_PHASE_ALL", "mla_extend_choose_path", "mla_extend_workspace_bytes", "mla_extend",
+    "MLA_EXTEND_AUTO", "MLA_EXTEND_ABSORBED", "MLA_EXTEND_EXPANDED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -28,11 +29,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_INSUFFICIENT_WORKSPACE = range(5)
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 MLA_PHASE_ABSORB, MLA_PHASE_ATTEND, MLA_PHASE_OUTPUT, MLA_PHASE_ALL = 1, 2, 4, 7
+MLA_EXTEND_AUTO, MLA_EXTEND_ABSORBED, MLA_EXTEND_EXPANDED = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
-    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
+    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_extend_choose_path",
+    "mla_extend_workspace_bytes", "mla_extend", "mla_status_string", "mla_last_error",
 )
 
 
@@ -81,6 +84,9 @@ def _load():
         "mla_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_decode_phases": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P,
                                     ctypes.c_uint32]),
+        "mla_extend_choose_path": (I32, [cfgp, I32, I32, I32, I32]),
+        "mla_extend_workspace_bytes": (S, [P, I32, I32, I32, I32, I32]),
+        "mla_extend": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
@@ -247,3 +253,33 @@ def mla_decode_phases(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, m
         int(max_seq_len), int(kv_chunk), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
         int(phases)), "mla_decode")
+
+
+def mla_extend_choose_path(cfg: MlaConfig, batch: int, total_q: int, max_q_len: int, max_seq_len: int) -> int:
+    """The form MLA_EXTEND_AUTO takes for these bounds (host only; -1 if invalid)."""
+    return int(lib.mla_extend_choose_path(ctypes.byref(cfg), int(batch), int(total_q), int(max_q_len),
+                                          int(max_seq_len)))
+
+
+def mla_extend_workspace_bytes(layer: Layer, batch: int, total_q: int, max_q_len: int, max_seq_len: int,
+                               path: int = MLA_EXTEND_AUTO) -> int:
+    return int(lib.mla_extend_workspace_bytes(layer.handle, int(batch), int(total_q), int(max_q_len),
+                                              int(max_seq_len), int(path)))
+
+
+def mla_extend(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_len: int, max_seq_len: int,
+               path: int = MLA_EXTEND_AUTO, workspace=None, stream=None):
+    """Prefill / chunked extend: the result of mla_decode, by the absorbed or
+    the expanded form (see include/mla.h)."""
+    dt = layer.cfg.torch_dtype
+    total_q = int(q.shape[0])
+    batch = int(seq_lens.shape[0])
+    if workspace is None:
+        n = mla_extend_workspace_bytes(layer, batch, total_q, max_q_len, max_seq_len, path)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_extend(
+        layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
+        int(max_seq_len), int(path), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "mla_extend")

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip"]
+SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip",
+           "extend.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -19,6 +19,7 @@ struct mla_layer {
   void* wdkv_t;    // rows n < D, k = d < d_model
   void* wuk_p;     // per head: rows j < d_c, k = i < d_nope
   void* wuv_p;     // per head: rows v < d_v, k = j < d_c
+  void* wukt_p;    // bf16: per head, rows i < d_nope, k = j < d_c (expanded path)
   mla::RopeFreq freq;   // rotary frequencies (bf16 layers)
   int num_cus;
 };
@@ -72,7 +73,7 @@ mla_status check_config(const mla_config* c) {
 int elem_of(const mla_config* c) { return c->dtype == MLA_DTYPE_BF16 ? 2 : 4; }
 
 struct FoldLayout {
-  size_t off_wdkv, off_wuk, off_wuv, total;
+  size_t off_wdkv, off_wuk, off_wuv, off_wukt, total;
 };
 
 FoldLayout fold_layout(const mla_config* c) {
@@ -82,7 +83,12 @@ FoldLayout fold_layout(const mla_config* c) {
   f.off_wdkv = 0;
   f.off_wuk = align256(D * c->d_model * e);
   f.off_wuv = f.off_wuk + align256((size_t)c->num_attention_heads * c->kv_lora_rank * c->qk_nope_head_dim * e);
-  f.total = f.off_wuv + align256((size_t)c->num_attention_heads * c->v_head_dim * c->kv_lora_rank * e);
+  f.off_wukt = f.off_wuv + align256((size_t)c->num_attention_heads * c->v_head_dim * c->kv_lora_rank * e);
+  // the transposed key weights of the expanded path (bf16 layers only)
+  f.total = f.off_wukt + (c->dtype == MLA_DTYPE_BF16
+                              ? align256((size_t)c->num_attention_heads * c->qk_nope_head_dim *
+                                         c->kv_lora_rank * e)
+                              : 0);
   return f;
 }
 
@@ -147,6 +153,48 @@ DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan
   return d;
 }
 
+// Expanded-path workspace: per-head content keys [batch][H][lmax][d_nope] and
+// values [batch][H][lmax/64][d_v][64], lmax = max_seq_len rounded up to 128.
+struct ExtendLayout {
+  int lmax;
+  size_t off_k, off_v, total;
+};
+
+ExtendLayout extend_layout(const mla_config& c, int batch, int max_seq_len) {
+  ExtendLayout e;
+  e.lmax = (max_seq_len + 127) / 128 * 128;
+  const size_t per = (size_t)batch * c.num_attention_heads * e.lmax * 2;
+  e.off_k = 0;
+  e.off_v = align256(per * c.qk_nope_head_dim);
+  e.total = e.off_v + align256(per * c.v_head_dim);
+  return e;
+}
+
+bool expanded_available(const mla_config& c) {
+  return c.dtype == MLA_DTYPE_BF16 && mla::extend_expanded_supported(c.qk_nope_head_dim, c.v_head_dim);
+}
+
+// Matrix-core work of the two forms for these host bounds (average keys per
+// query taken as max_seq_len - max_q_len / 2, the causal mean of a chunk that
+// ends the sequence).  Absorbed: every query is folded into latent space and
+// back (2 d_c (d_nope + d_v) per query and head) and scored at width
+// 2 d_c + d_rope per key.  Expanded: every cached token is expanded once per
+// head (2 d_c (d_nope + d_v)) and scored at width d_nope + d_rope + d_v.
+// The expanded count is weighted by kExpandedWeight, the ratio of the two
+// paths' measured matrix-core efficiencies.
+constexpr double kExpandedWeight = 1.0;
+
+int choose_extend_path(const mla_config& c, int batch, int total_q, int max_q_len, int max_seq_len) {
+  if (!expanded_available(c)) return MLA_EXTEND_ABSORBED;
+  const double H = c.num_attention_heads, dc = c.kv_lora_rank, dr = c.qk_rope_head_dim;
+  const double dn = c.qk_nope_head_dim, dv = c.v_head_dim;
+  const double keys = (double)max_seq_len - 0.5 * (double)max_q_len;
+  const double absorbed = (double)total_q * H * (2.0 * dc * (dn + dv) + 2.0 * (2.0 * dc + dr) * keys);
+  const double expanded = (double)batch * max_seq_len * H * 2.0 * dc * (dn + dv) +
+                          (double)total_q * H * 2.0 * (dn + dr + dv) * keys;
+  return expanded * kExpandedWeight < absorbed ? MLA_EXTEND_EXPANDED : MLA_EXTEND_ABSORBED;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -200,11 +248,12 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
   L->wdkv_t = (char*)folded + f.off_wdkv;
   L->wuk_p = (char*)folded + f.off_wuk;
   L->wuv_p = (char*)folded + f.off_wuv;
+  L->wukt_p = L->elem == 2 ? (char*)folded + f.off_wukt : nullptr;
   L->num_cus = ncu;
   for (int i = 0; i < mla::kRopePairs; ++i)
     L->freq.theta[i] = pow((double)cfg->rope_base, -2.0 * i / (double)cfg->qk_rope_head_dim);
-  mla::launch_pack(L->elem, w_dkv, w_uk, w_uv, L->wdkv_t, L->wuk_p, L->wuv_p, cfg->d_model,
-                   cfg->num_attention_heads, cfg->qk_nope_head_dim, cfg->v_head_dim,
+  mla::launch_pack(L->elem, w_dkv, w_uk, w_uv, L->wdkv_t, L->wuk_p, L->wuv_p, L->wukt_p,
+                   cfg->d_model, cfg->num_attention_heads, cfg->qk_nope_head_dim, cfg->v_head_dim,
                    cfg->kv_lora_rank, cfg->qk_rope_head_dim, (hipStream_t)hip_stream);
   st = hip_check("fold launch");
   if (st != MLA_OK) {
@@ -338,6 +387,68 @@ mla_status mla_decode(const mla_layer* L, const void* q, const int32_t* cu_q, co
   return mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
                            max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
                            hip_stream, MLA_PHASE_ALL);
+}
+
+int32_t mla_extend_choose_path(const mla_config* cfg, int32_t batch, int32_t total_q, int32_t max_q_len,
+                               int32_t max_seq_len) {
+  if (check_config(cfg) != MLA_OK) return -1;
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len ||
+      (int64_t)total_q > (int64_t)batch * max_q_len)
+    return -1;
+  return choose_extend_path(*cfg, batch, total_q, max_q_len, max_seq_len);
+}
+
+size_t mla_extend_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_q, int32_t max_q_len,
+                                  int32_t max_seq_len, int32_t path) {
+  if (!L) return 0;
+  if (path == MLA_EXTEND_AUTO) path = mla_extend_choose_path(&L->cfg, batch, total_q, max_q_len, max_seq_len);
+  if (path == MLA_EXTEND_ABSORBED)
+    return mla_decode_workspace_bytes(L, batch, total_q, max_q_len, max_seq_len, 0);
+  if (path != MLA_EXTEND_EXPANDED || !expanded_available(L->cfg)) return 0;
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len) return 0;
+  return extend_layout(L->cfg, batch, max_seq_len).total;
+}
+
+mla_status mla_extend(const mla_layer* L, const void* q, const int32_t* cu_q, const int32_t* seq_lens,
+                      const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t total_q,
+                      int32_t max_q_len, int32_t max_seq_len, int32_t path, const void* cache,
+                      int64_t num_pages, void* out, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (path != MLA_EXTEND_AUTO && path != MLA_EXTEND_ABSORBED && path != MLA_EXTEND_EXPANDED)
+    return fail(MLA_ERR_INVALID_ARG, "mla_extend: unknown path %d", path);
+  if (!q || !cu_q || !seq_lens || !page_table || !cache || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_extend: null pointer argument");
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len || max_pages <= 0 ||
+      num_pages <= 0 || (int64_t)max_pages * L->cfg.page_size < max_seq_len ||
+      (int64_t)total_q > (int64_t)batch * max_q_len)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_extend: bad sizes (batch %d, total_q %d, max_q_len %d, max_seq_len %d, max_pages %d)",
+                batch, total_q, max_q_len, max_seq_len, max_pages);
+  if (path == MLA_EXTEND_AUTO) path = choose_extend_path(L->cfg, batch, total_q, max_q_len, max_seq_len);
+  if (path == MLA_EXTEND_ABSORBED)
+    return mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                             max_seq_len, 0, cache, num_pages, out, workspace, workspace_bytes, hip_stream,
+                             MLA_PHASE_ALL);
+  const mla_config& c = L->cfg;
+  if (!expanded_available(c))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_extend: the expanded path needs a bf16 layer with qk_nope_head_dim and v_head_dim "
+                "each 64 or 128");
+  const ExtendLayout e = extend_layout(c, batch, max_seq_len);
+  if (workspace_bytes < e.total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "extend workspace holds %zu bytes, %zu needed",
+                workspace_bytes, e.total);
+  if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  const int H = c.num_attention_heads;
+  mla::launch_expand_kv(cache, seq_lens, page_table, max_pages, batch, H, c.qk_nope_head_dim, c.v_head_dim,
+                        c.page_size, e.lmax, L->wukt_p, L->wuv_p, ws + e.off_k, ws + e.off_v, st);
+  mla::launch_extend_attn(q, ws + e.off_k, ws + e.off_v, cache, cu_q, seq_lens, page_table, max_pages, batch,
+                          max_q_len, H, c.qk_nope_head_dim, c.v_head_dim, c.page_size, e.lmax, L->freq,
+                          L->scale, out, st);
+  return hip_check("extend launch");
 }
 
 }  // extern "C"

@@ -10,11 +10,12 @@ namespace mla {
 
 // ---- fold (pack) ---------------------------------------------------------
 // bf16 (elem 2): fragment-tiled wdkv (rows n, k = d), wuk[h] (rows j, k = i),
-// wuv[h] (rows v, k = j).  fp32 (elem 4): wdkv_t[n][d] = w_dkv[d][n];
-// wuk_p[h][j][i] = w_uk[j][h*dn+i]; wuv_p[h][v][j] = w_uv[j][h*dv+v].
+// wuv[h] (rows v, k = j), wukt[h] (rows i, k = j).  fp32 (elem 4):
+// wdkv_t[n][d] = w_dkv[d][n]; wuk_p[h][j][i] = w_uk[j][h*dn+i];
+// wuv_p[h][v][j] = w_uv[j][h*dv+v]; wukt unused (may be null).
 void launch_pack(int elem, const void* w_dkv, const void* w_uk, const void* w_uv, void* wdkv_t,
-                 void* wuk_p, void* wuv_p, int d_model, int H, int dn, int dv, int dc, int dr,
-                 hipStream_t st);
+                 void* wuk_p, void* wuv_p, void* wukt, int d_model, int H, int dn, int dv, int dc,
+                 int dr, hipStream_t st);
 
 // ---- append --------------------------------------------------------------
 // part[ks][m][n] = sum over the ks-th k chunk of x[m][k] * wt[n][k].
@@ -65,5 +66,26 @@ void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cach
 void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,
                     void* olat, hipStream_t st);
+
+// ---- expanded prefill / chunked extend (bf16 layers) ------------------------
+// Whether the expanded kernels are built for these head widths.
+bool extend_expanded_supported(int dn, int dv);
+// Per head, materialise the content keys and the values of every cached token
+// of every sequence from its latent row:
+//   kexp[b][h][t][i]                  = sum_j c_t[j] W_uk[j][h*dn + i]
+//   vexp[b][h][t/64][v][perm(t % 64)] = sum_j c_t[j] W_uv[j][h*dv + v]
+// for t < round_up(seq_len_b, 128) (rows past seq_len_b repeat the last row);
+// perm swaps bits 2 and 3 of the token index inside each group of 16.
+// lmax (a multiple of 128) is the token stride of one (sequence, head).
+void launch_expand_kv(const void* cache, const int32_t* seq_lens, const int32_t* page_table,
+                      int max_pages, int batch, int H, int dn, int dv, int page_size, int lmax,
+                      const void* wukt, const void* wuv, void* kexp, void* vexp, hipStream_t st);
+// Causal flash attention of every query over its sequence's expanded keys
+// and values: out[t][h][:] = softmax(scale * q_t . k) V.
+void launch_extend_attn(const void* q, const void* kexp, const void* vexp, const void* cache,
+                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
+                        int max_pages, int batch, int max_q_len, int H, int dn, int dv,
+                        int page_size, int lmax, const RopeFreq& freq, float scale, void* out,
+                        hipStream_t st);
 
 }  // namespace mla

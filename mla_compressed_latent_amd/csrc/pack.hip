@@ -7,7 +7,10 @@
 // contraction index as k:
 //   wdkv[n][d]      rows n < d_c + d_rope, k = d < d_model     (append)
 //   wuk[h][j][i]    per head, rows j < d_c, k = i < d_nope      (absorb)
-//   wuv[h][v][j]    per head, rows v < d_v, k = j < d_c         (output)
+//   wuv[h][v][j]    per head, rows v < d_v, k = j < d_c         (output, and
+//                   the value expansion of the expanded prefill path)
+//   wukt[h][i][j]   per head, rows i < d_nope, k = j < d_c      (key expansion
+//                   of the expanded prefill path)
 // fp32 layers keep plain row-major transposes with the contraction index
 // contiguous (the fp32 kernels read them one element at a time).
 #include "common.hpp"
@@ -20,13 +23,15 @@ namespace {
 // fine for a one-time repack.
 __global__ void pack_bf16_kernel(const bf16* __restrict__ w_dkv, const bf16* __restrict__ w_uk,
                                  const bf16* __restrict__ w_uv, bf16* __restrict__ wdkv,
-                                 bf16* __restrict__ wuk, bf16* __restrict__ wuv, int d_model, int H,
-                                 int dn, int dv, int dc, int dr) {
+                                 bf16* __restrict__ wuk, bf16* __restrict__ wuv,
+                                 bf16* __restrict__ wukt, int d_model, int H, int dn, int dv, int dc,
+                                 int dr) {
   const int D = dc + dr;
   const int64_t n1 = (int64_t)D * d_model;
   const int64_t n2 = (int64_t)H * dc * dn;
   const int64_t n3 = (int64_t)H * dv * dc;
-  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n1 + n2 + n3;
+  const int64_t n4 = (int64_t)H * dn * dc;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n1 + n2 + n3 + n4;
        o += (int64_t)gridDim.x * blockDim.x) {
     // invert tiled_index within one matrix of K columns
     auto untile = [](int64_t p, int K, int* row, int* k) {
@@ -45,11 +50,16 @@ __global__ void pack_bf16_kernel(const bf16* __restrict__ w_dkv, const bf16* __r
       const int h = (int)(p / per);
       untile(p % per, dn, &row, &k);                      // row = j, k = i
       wuk[p] = w_uk[(int64_t)row * H * dn + (int64_t)h * dn + k];
-    } else {
+    } else if (o < n1 + n2 + n3) {
       const int64_t p = o - n1 - n2, per = (int64_t)dv * dc;
       const int h = (int)(p / per);
       untile(p % per, dc, &row, &k);                      // row = v, k = j
       wuv[p] = w_uv[(int64_t)k * H * dv + (int64_t)h * dv + row];
+    } else {
+      const int64_t p = o - n1 - n2 - n3, per = (int64_t)dn * dc;
+      const int h = (int)(p / per);
+      untile(p % per, dc, &row, &k);                      // row = i, k = j
+      wukt[p] = w_uk[(int64_t)k * H * dn + (int64_t)h * dn + row];
     }
   }
 }
@@ -82,13 +92,13 @@ __global__ void pack_f32_kernel(const float* __restrict__ w_dkv, const float* __
 }  // namespace
 
 void launch_pack(int elem, const void* w_dkv, const void* w_uk, const void* w_uv, void* wdkv,
-                 void* wuk, void* wuv, int d_model, int H, int dn, int dv, int dc, int dr,
-                 hipStream_t st) {
+                 void* wuk, void* wuv, void* wukt, int d_model, int H, int dn, int dv, int dc,
+                 int dr, hipStream_t st) {
   const int threads = 256, blocks = 2048;
   if (elem == 2) {
     pack_bf16_kernel<<<blocks, threads, 0, st>>>(
         (const bf16*)w_dkv, (const bf16*)w_uk, (const bf16*)w_uv, (bf16*)wdkv, (bf16*)wuk,
-        (bf16*)wuv, d_model, H, dn, dv, dc, dr);
+        (bf16*)wuv, (bf16*)wukt, d_model, H, dn, dv, dc, dr);
   } else {
     pack_f32_kernel<<<blocks, threads, 0, st>>>(
         (const float*)w_dkv, (const float*)w_uk, (const float*)w_uv, (float*)wdkv, (float*)wuk,

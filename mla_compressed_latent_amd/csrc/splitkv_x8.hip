@@ -63,7 +63,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
   const int row_base = rq * kX8Rows;
   const int tok_begin = s * chunk;
   if (row_base >= R || tok_begin >= L) return;
-  const int tok_end = min(tok_begin + chunk, L);
+  // keys past the last visible position of the block's last row are masked
+  // for every row of the block: stop there, keeping at least one token so the
+  // split still writes its (empty) partial
+  const int last_vis = L - Lq + (min(row_base + kX8Rows, R) - 1) / H;
+  const int tok_end = min(min(tok_begin + chunk, L), max(tok_begin + 1, last_vis + 1));
   const int ntiles = (tok_end - tok_begin + kTileTok - 1) / kTileTok;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -125,6 +125,8 @@ class Workload:
     max_q_len: int = 1                # ragged: q_len ~ U{1..max_q_len}
     spare_page_frac: float = 0.0
     description: str = ""
+    kind: str = "decode"              # "decode": the step is append + mla_decode;
+                                      # "extend": append + mla_extend (long chunks)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -255,6 +257,15 @@ WORKLOADS = {
         fixed_prefix=None, max_prefix=32768, fixed_q_len=None, max_q_len=2, spare_page_frac=0.05,
         description="bf16; DeepSeek-V2 shape, 256 sequences, prefix ~ U[1, 32768], q_len ~ U{1,2}, "
                     "64-token pages under a random page table, new tokens appended first"),
+    "dsv2_extend_b4_p3072_c1024": Workload(
+        "dsv2_extend_b4_p3072_c1024", DSV2, batch=4, seed=6, prefix_source="hidden", fixed_prefix=3072,
+        fixed_q_len=1024, max_q_len=1024, kind="extend",
+        description="bf16; DeepSeek-V2 shape, chunked extend: 4 sequences, cached prefix 3072, "
+                    "a 1024-token chunk appended and attended causally (context 4096)"),
+    "dsv2_prefill_b2_4096": Workload(
+        "dsv2_prefill_b2_4096", DSV2, batch=2, seed=7, prefix_source="hidden", fixed_prefix=0,
+        fixed_q_len=4096, max_q_len=4096, kind="extend",
+        description="bf16; DeepSeek-V2 shape, prefill: 2 sequences of 4096 new tokens, empty cache"),
 }
 
 

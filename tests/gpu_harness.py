@@ -108,6 +108,14 @@ class GpuCase:
                             self.max_q_len, self.max_seq_len, kv_chunk=kv_chunk, stream=stream)
         return out
 
+    def extend(self, path, out=None, workspace=None, stream=None):
+        s = self.wl.shape
+        if out is None:
+            out = torch.empty((self.q.shape[0], s.H, s.d_v), dtype=self.dt, device=self.q_dev.device)
+        self.mla.mla_extend(self.layer, self.q_dev, self.cu_q, self.seq_lens, self.page_table, self.cache, out,
+                            self.max_q_len, self.max_seq_len, path=path, workspace=workspace, stream=stream)
+        return out
+
     def logical_rows(self, b):
         """Sequence b's cached rows as stored on the GPU (for placement checks)."""
         ps = self.wl.shape.page_size
@@ -139,6 +147,18 @@ def oracle_outputs(wl: Workload, b: int, heads=None, w_dkv=None, w_uk=None, w_uv
     scale = mla_oracle.default_scale(s.d_nope, s.d_rope)
     return mla_oracle.attend_sequence(wl.queries(b), cache, w_uk, w_uv, s.H, s.d_nope, s.d_v, s.rope_base,
                                       scale, heads)
+
+
+def oracle_query(wl: Workload, b: int, i: int, heads, cache: np.ndarray, q_b: np.ndarray, w_uk, w_uv) -> np.ndarray:
+    """Oracle output [len(heads)][d_v] of query i of sequence b alone: the
+    query sits at position L - q_len + i, so it is the last query of the
+    oracle's call over rows 0 .. that position."""
+    s = wl.shape
+    L, lq = cache.shape[0], q_b.shape[0]
+    pos = L - lq + i
+    scale = mla_oracle.default_scale(s.d_nope, s.d_rope)
+    return mla_oracle.attend_sequence(q_b[i:i + 1], cache[:pos + 1], w_uk, w_uv, s.H, s.d_nope, s.d_v,
+                                      s.rope_base, scale, heads)[0]
 
 
 def errors(gpu: np.ndarray, ref: np.ndarray):

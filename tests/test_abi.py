@@ -54,9 +54,14 @@ def test_cache_bytes_per_token(mla):
 
 
 def test_folded_bytes_covers_packed_weights(mla):
+    # W_dkv, W_uk, W_uv and (bf16) the transposed W_uk of the expanded path
     n = mla.mla_folded_bytes(_cfg(mla))
-    w = (5120 * 576 + 512 * 128 * 128 * 2) * 2
-    assert w <= n < w + 3 * 256
+    w = (5120 * 576 + 512 * 128 * 128 * 3) * 2
+    assert w <= n < w + 4 * 256
+    tiny = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                v_head_dim=16, kv_lora_rank=32, dtype=0)
+    w = (64 * 40 + 32 * 4 * 16 * 2) * 4
+    assert w <= mla.mla_folded_bytes(tiny) < w + 3 * 256
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -99,3 +104,35 @@ def test_null_and_size_errors(mla):
 def test_status_strings(mla):
     assert [mla.mla_status_string(i) for i in range(5)] == [
         "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_HIP", "MLA_ERR_INSUFFICIENT_WORKSPACE"]
+
+
+def test_extend_path_choice(mla):
+    """AUTO picks the absorbed form for decode-sized query counts and the
+    expanded form for long chunks; it never picks a form the layer lacks."""
+    ABS, EXP = mla.MLA_EXTEND_ABSORBED, mla.MLA_EXTEND_EXPANDED
+    dsv2 = _cfg(mla)
+    for q in (1, 2, 8):
+        assert mla.mla_extend_choose_path(dsv2, 32, 32 * q, q, 4096) == ABS
+    assert mla.mla_extend_choose_path(dsv2, 4, 4 * 1024, 1024, 4096) == EXP
+    assert mla.mla_extend_choose_path(dsv2, 2, 2 * 4096, 4096, 4096) == EXP
+    # monotone in the chunk length at a fixed context: one crossover
+    picks = [mla.mla_extend_choose_path(dsv2, 1, q, q, 8192) for q in range(1, 8193, 97)]
+    assert picks[0] == ABS and picks[-1] == EXP
+    assert all(a <= b for a, b in zip(picks, picks[1:]))
+    # no expanded kernels for fp32 layers or other head widths
+    tiny = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                v_head_dim=16, kv_lora_rank=32, dtype=0)
+    assert mla.mla_extend_choose_path(tiny, 1, 4096, 4096, 4096) == ABS
+    assert mla.mla_extend_choose_path(_cfg(mla, qk_nope_head_dim=96), 1, 4096, 4096, 4096) == ABS
+    # invalid bounds
+    assert mla.mla_extend_choose_path(dsv2, 0, 1, 1, 1) == -1
+    assert mla.mla_extend_choose_path(dsv2, 2, 1, 1, 1) == -1          # total_q < batch
+    assert mla.mla_extend_choose_path(dsv2, 1, 5, 4, 8) == -1          # total_q > batch * max_q_len
+    assert mla.mla_extend_choose_path(dsv2, 1, 8, 8, 4) == -1          # max_seq_len < max_q_len
+    assert mla.mla_extend_choose_path(_cfg(mla, page_size=48), 1, 1, 1, 1) == -1
+
+
+def test_extend_rejects_null_layer(mla):
+    assert mla.lib.mla_extend_workspace_bytes(None, 1, 1, 1, 1, 0) == 0
+    st = mla.lib.mla_extend(None, None, None, None, None, 1, 1, 1, 1, 1, 0, None, 1, None, None, 0, None)
+    assert st == 1 and "null" in mla.mla_last_error()
