@@ -238,7 +238,7 @@ int32_t mla_extend_choose_path(const mla_config* cfg, int32_t batch, int32_t tot
 
 /* Workspace mla_extend needs for these bounds and path (AUTO resolved as
  * above).  Expanded: batch * H * lmax * (d_nope + d_v) * 2 bytes (plus
- * alignment), lmax = max_seq_len rounded up to a multiple of 128.  0 on
+ * alignment), lmax = max_seq_len rounded up to a multiple of 256.  0 on
  * invalid arguments or when the path is unavailable for the layer. */
 size_t mla_extend_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
                                   int32_t max_q_len, int32_t max_seq_len, int32_t path);

@@ -154,7 +154,8 @@ DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan
 }
 
 // Expanded-path workspace: per-head content keys [batch][H][lmax][d_nope] and
-// values [batch][H][lmax/64][d_v][64], lmax = max_seq_len rounded up to 128.
+// values [batch][H][lmax/64][d_v][64], lmax = max_seq_len rounded up to 256
+// (the expansion kernel's token block).
 struct ExtendLayout {
   int lmax;
   size_t off_k, off_v, total;
@@ -162,7 +163,7 @@ struct ExtendLayout {
 
 ExtendLayout extend_layout(const mla_config& c, int batch, int max_seq_len) {
   ExtendLayout e;
-  e.lmax = (max_seq_len + 127) / 128 * 128;
+  e.lmax = (max_seq_len + 255) / 256 * 256;
   const size_t per = (size_t)batch * c.num_attention_heads * e.lmax * 2;
   e.off_k = 0;
   e.off_v = align256(per * c.qk_nope_head_dim);

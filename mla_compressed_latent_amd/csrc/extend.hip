@@ -14,17 +14,17 @@
 // kernels, both on the matrix cores, every operand streamed HBM -> LDS as
 // whole 1 KB MFMA fragments by the LDS-DMA path:
 //
-//  expand_kv_kernel   one workgroup per (sequence, head, 128 tokens):
-//                     K_h = C W_uk_h (stored token-major) and V_h = C W_uv_h
-//                     (stored transposed, in 64-token tiles).
-//  extend_attn_kernel one workgroup per (sequence, head, 128 queries), one
+//  expand_kv_kernel   one workgroup per (sequence, head, 256 tokens):
+//                     K_h = C W_uk_h and V_h = C W_uv_h, stored per 64-token
+//                     tile as the attention kernel's operand fragments, so
+//                     its copies are contiguous 1 KB reads.
+//  extend_attn_kernel one workgroup per (sequence, head, 256 queries), one
 //                     wave per 32 queries: causal flash attention.  Scores
 //                     are formed transposed (S^T = K Q^T, tokens down the
 //                     rows) so each lane owns one query column, the softmax
 //                     runs in registers, and the probabilities are already
-//                     the B operand of O^T = V^T P^T.  The value tiles are
-//                     stored with token bits 2 and 3 swapped inside each group
-//                     of 16 so that the A operand matches that register order.
+//                     the B operand of O^T = V^T P^T.  The value fragments
+//                     hold their tokens in that register order.
 //
 // The rotated position key is read from the cache itself (one copy for all
 // heads, "The code", decoupled_score); only the content key and the value
@@ -41,22 +41,17 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f);
 
 __device__ __forceinline__ void wait_dma_ahead(int ahead, int per_stage) {
   // s_waitcnt takes an immediate: the counts used here are 0 .. 2 stages of
-  // at most 10 copies each.
-  const int n = ahead * per_stage;
-  switch (n) {
+  // at most 5 copies each.
+  switch (ahead * per_stage) {
     case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
     case 4: wait_vmcnt<4>(); break;
     case 5: wait_vmcnt<5>(); break;
     case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
     case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
     case 10: wait_vmcnt<10>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 16: wait_vmcnt<16>(); break;
-    case 18: wait_vmcnt<18>(); break;
-    case 20: wait_vmcnt<20>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -64,35 +59,37 @@ __device__ __forceinline__ void wait_dma_ahead(int ahead, int per_stage) {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // ================================================================ expansion
-constexpr int kExpTok = 128;                 // tokens per workgroup
+constexpr int kExpTok = 256;                 // tokens per workgroup, 64 per wave pair
 constexpr int kExpStep = 32;                 // latent columns per pipeline stage (two k-steps)
 constexpr int kExpStages = kDC / kExpStep;   // 16
 constexpr int kExpBuf = 4;                   // stage buffers: one being read, three in flight
+constexpr int kExpWaves = 8;
 
 template <int DN, int DV>
 struct ExpandDims {
-  static constexpr int kFragC = (kExpTok / 32) * 2;   // cache-row fragments per stage
+  static constexpr int kFragC = kExpTok * kExpStep * 2 / 1024;   // 1 KB slots of cache rows per stage
   static constexpr int kFragK = (DN / 32) * 2;        // W_uk_h^T fragments per stage
   static constexpr int kFragV = (DV / 32) * 2;        // W_uv_h fragments per stage
   static constexpr int kFrag = kFragC + kFragK + kFragV;
-  static_assert(kFrag % 4 == 0, "fragments must split evenly over four waves");
-  static constexpr int kDma = kFrag / 4;
-  static constexpr int kAcc = (DN > DV ? DN : DV) / 32 * 2;
+  // copies per wave and stage; slots past kFrag repeat fragment 0 (unused)
+  static constexpr int kDma = (kFrag + kExpWaves - 1) / kExpWaves;
+  static constexpr int kSlots = kDma * kExpWaves;
 };
 
-// Waves 0, 1: keys of tokens t0 + 64 w .. + 63, accumulators K^T[i][t]
-// (A = W_uk_h^T fragment, B = cache-row fragment).  Waves 2, 3: values of
-// the same token halves, accumulators V[t][v] (A = cache rows, B = W_uv_h).
+// Waves 0-3: keys of tokens t0 + 64 w .. + 63, accumulators K^T[i][t]
+// (A = W_uk_h^T fragment, B = cache-row fragment).  Waves 4-7: values of the
+// same token quarters, accumulators V[t][v] (A = cache rows, B = W_uv_h).
 // Both operands are d_c-contiguous, so the two products use the same
-// fragments with the roles of A and B swapped.
+// fragments with the roles of A and B swapped.  Two waves share each SIMD,
+// so one wave's waits and stores overlap the other's matrix work.
 template <int DN, int DV>
-__global__ __launch_bounds__(256, 1) void expand_kv_kernel(
+__global__ __launch_bounds__(512, 1) void expand_kv_kernel(
     const bf16* __restrict__ cache, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, int max_pages, int batch, int H, int page_size,
     int lmax, const bf16* __restrict__ wukt, const bf16* __restrict__ wuv,
     bf16* __restrict__ kexp, bf16* __restrict__ vexp) {
   using Dm = ExpandDims<DN, DV>;
-  __shared__ __attribute__((aligned(1024))) bf16 sbuf[kExpBuf][Dm::kFrag * 512];
+  __shared__ __attribute__((aligned(1024))) bf16 sbuf[kExpBuf][Dm::kSlots * 512];
 
   const int ntt = lmax / kExpTok;
   const int nblocks = batch * H * ntt;
@@ -115,17 +112,20 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(
   uint32_t stride[Dm::kDma];
 #pragma unroll
   for (int u = 0; u < Dm::kDma; ++u) {
-    const int f = wave * Dm::kDma + u;
+    int f = wave * Dm::kDma + u;
+    if (f >= Dm::kFrag) f = 0;
     if (f < Dm::kFragC) {
-      // 32 tokens of one page (pages hold a multiple of 64 tokens); rows past
-      // the sequence repeat its last row
-      const int rb = f >> 1, s = f & 1;
-      const int tf = min(t0 + 32 * rb, L - 1);
+      // slot f: tokens t0 + 16 f .. + 15 (one page: pages hold a multiple of
+      // 64 tokens), the stage's 64 bytes of each row as four 16-byte chunks,
+      // lane l at row l / 4, position l % 4 holding chunk (l % 4) ^ swizzle.
+      // Rows past the sequence repeat its last row.
+      const int tf = min(t0 + 16 * f, L - 1);
       const int page = __builtin_amdgcn_readfirstlane(
           page_table[(int64_t)b * max_pages + tf / page_size]);
-      const int tl = min(t0 + 32 * rb + l32, L - 1);
+      const int tl = min(t0 + 16 * f + (lane >> 2), L - 1);
+      const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
       src[u] = reinterpret_cast<const char*>(cache + (int64_t)page * page_size * kD);
-      voff[u] = (uint32_t)(((tl % page_size) * kD + 16 * s + 8 * hh) * 2);
+      voff[u] = (uint32_t)(((tl % page_size) * kD + 8 * chunk) * 2);
       stride[u] = kExpStep * 2;
     } else if (f < Dm::kFragC + Dm::kFragK) {
       const int g = f - Dm::kFragC, ib = g >> 1, s = g & 1;
@@ -142,94 +142,119 @@ __global__ __launch_bounds__(256, 1) void expand_kv_kernel(
     }
   }
   auto issue = [&](int st) {
-    const uint32_t dst = lds0 + (uint32_t)(((st % kExpBuf) * Dm::kFrag + wave * Dm::kDma) * 1024);
+    const uint32_t dst = lds0 + (uint32_t)(((st % kExpBuf) * Dm::kSlots + wave * Dm::kDma) * 1024);
 #pragma unroll
     for (int u = 0; u < Dm::kDma; ++u) dma16(src[u] + st * stride[u], voff[u], dst + u * 1024);
   };
-
-  f32x16 acc[Dm::kAcc];
-#pragma unroll
-  for (int i = 0; i < Dm::kAcc; ++i) acc[i] = zero_f32x16();
-  const bool kwave = wave < 2;
-  const int th = wave & 1;
+  // stage st is in LDS for every wave, and every wave has finished reading
+  // stage st - 1 (whose buffer the copies issued next overwrite)
+  auto stage_ready = [&](int st) -> const bf16x8* {
+    wait_dma_ahead(min(kExpBuf - 2, kExpStages - 1 - st), Dm::kDma);
+    wait_lds();
+    __syncthreads();
+    if (st + kExpBuf - 1 < kExpStages) issue(st + kExpBuf - 1);
+    return reinterpret_cast<const bf16x8*>(&sbuf[st % kExpBuf][0]);
+  };
 
 #pragma unroll
   for (int st = 0; st < kExpBuf - 1; ++st) issue(st);
-  for (int st = 0; st < kExpStages; ++st) {
-    wait_dma_ahead(min(kExpBuf - 2, kExpStages - 1 - st), Dm::kDma);
-    wait_lds();
-    __syncthreads();   // stage st landed for every wave; stage st-1 fully read
-    if (st + kExpBuf - 1 < kExpStages) issue(st + kExpBuf - 1);
-    const bf16x8* fr = reinterpret_cast<const bf16x8*>(&sbuf[st % kExpBuf][0]);
+  const int64_t bh = (int64_t)b * H + h;
+  const int th = wave & 3;
+  // cache-row operand of row block j: row r = 64 th + 32 j + l32 of the tile,
+  // chunk c at 16-byte position 4 r + (c ^ ((r >> 2) & 3)) -- sixteen
+  // consecutive rows read one chunk each from sixteen different bank groups
+  const int crow[2] = {(64 * th + l32) * 4, (64 * th + 32 + l32) * 4};
+  const int cswz = (l32 >> 2) & 3;
+  const int tile0 = (t0 >> 6) + th;   // this wave's 64-token tile
+
+  if (wave < 4) {
+    f32x16 acc[DN / 32][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 c[2];
+    for (int i = 0; i < DN / 32; ++i)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) c[tb] = fr[((2 * th + tb) * 2 + s) * 64 + lane];
-      if (kwave) {
+      for (int j = 0; j < 2; ++j) acc[i][j] = zero_f32x16();
+    for (int st = 0; st < kExpStages; ++st) {
+      const bf16x8* fr = stage_ready(st);
 #pragma unroll
-        for (int ib = 0; ib < DN / 32; ++ib) {
-          const bf16x8 a = fr[(Dm::kFragC + ib * 2 + s) * 64 + lane];
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 c[2];
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) acc[ib * 2 + tb] = mfma32(a, c[tb], acc[ib * 2 + tb]);
-        }
-      } else {
+        for (int j = 0; j < 2; ++j) c[j] = fr[crow[j] + ((2 * s + hh) ^ cswz)];
 #pragma unroll
-        for (int vb = 0; vb < DV / 32; ++vb) {
-          const bf16x8 w = fr[(Dm::kFragC + Dm::kFragK + vb * 2 + s) * 64 + lane];
+        for (int i = 0; i < DN / 32; ++i) {
+          const bf16x8 a = fr[(Dm::kFragC + i * 2 + s) * 64 + lane];
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            acc[tb * (DV / 32) + vb] = mfma32(c[tb], w, acc[tb * (DV / 32) + vb]);
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a, c[j], acc[i][j]);
         }
       }
     }
-  }
-
-  const int64_t bh = (int64_t)b * H + h;
-  if (kwave) {
-    // K^T accumulator: element r is key column 32 ib + acc_row32(r), token
-    // t0 + 64 th + 32 tb + l32; four consecutive r are four adjacent columns
+    // K^T accumulator: element r is key column d = 32 i + acc_row32(r) of
+    // token 32 j + l32 of the wave's tile.  Stored as the attention kernel's
+    // score-operand fragments: fragment (j, d / 16) of the tile, lane
+    // l32 + 32 ((d / 8) & 1), element d % 8 -- four consecutive r are four
+    // consecutive elements, and the wave's stores cover whole 512-byte runs.
 #pragma unroll
-    for (int ib = 0; ib < DN / 32; ++ib)
+    for (int i = 0; i < DN / 32; ++i)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int t = t0 + 64 * th + 32 * tb + l32;
-        bf16* row = kexp + (bh * lmax + t) * DN + 32 * ib + 4 * hh;
+      for (int j = 0; j < 2; ++j) {
+        bf16* tb = kexp + (((bh * (lmax / 64) + tile0) * 2 + j) * (DN / 16)) * 512;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x16& a = acc[ib * 2 + tb];
-          bf16x4 v = {from_f32<bf16>(a[4 * j]), from_f32<bf16>(a[4 * j + 1]),
-                      from_f32<bf16>(a[4 * j + 2]), from_f32<bf16>(a[4 * j + 3])};
-          *reinterpret_cast<bf16x4*>(row + 8 * j) = v;
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[i][j];
+          bf16x4 v = {from_f32<bf16>(a[4 * q]), from_f32<bf16>(a[4 * q + 1]),
+                      from_f32<bf16>(a[4 * q + 2]), from_f32<bf16>(a[4 * q + 3])};
+          *reinterpret_cast<bf16x4*>(tb + ((2 * i + (q >> 1)) * 64 + l32 + 32 * (q & 1)) * 8 + 4 * hh) = v;
         }
       }
   } else {
-    // V accumulator: element r is token 32 tb + acc_row32(r) of the 64-token
-    // tile, value column 32 vb + l32.  With bits 2 and 3 of the token index
-    // swapped inside each 16-token group, elements 0..7 land at tile
-    // positions 32 tb + 8 hh + 0..7 and elements 8..15 sixteen further on.
-    const int tile = tt * 2 + th;
+    f32x16 acc[2][DV / 32];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int vb = 0; vb < DV / 32; ++vb) {
-        const f32x16& a = acc[tb * (DV / 32) + vb];
-        bf16* dst = vexp + ((bh * (lmax / 64) + tile) * DV + 32 * vb + l32) * 64 + 32 * tb + 8 * hh;
+      for (int i = 0; i < DV / 32; ++i) acc[j][i] = zero_f32x16();
+    for (int st = 0; st < kExpStages; ++st) {
+      const bf16x8* fr = stage_ready(st);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 c[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) c[j] = fr[crow[j] + ((2 * s + hh) ^ cswz)];
+#pragma unroll
+        for (int i = 0; i < DV / 32; ++i) {
+          const bf16x8 w = fr[(Dm::kFragC + Dm::kFragK + i * 2 + s) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[j][i] = mfma32(c[j], w, acc[j][i]);
+        }
+      }
+    }
+    // V accumulator: element r is token 32 j + acc_row32(r) of the wave's
+    // tile, value column 32 i + l32.  Stored as the attention kernel's
+    // value-operand fragments (A operand of O^T = V^T P^T): fragment (i, k)
+    // of the tile, lane l, eight tokens whose order matches the probability
+    // registers -- elements 0..7 of the accumulator are fragment k = 2 j,
+    // elements 8..15 fragment 2 j + 1, each one 16-byte store per lane.
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i) {
+        const f32x16& a = acc[j][i];
+        bf16* dst = vexp + ((((bh * (lmax / 64) + tile0) * (DV / 32) + i) * 4 + 2 * j) * 64 + lane) * 8;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           bf16x8 v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = from_f32<bf16>(a[8 * g + e]);
-          *reinterpret_cast<bf16x8*>(dst + 16 * g) = v;
+          *reinterpret_cast<bf16x8*>(dst + g * 512) = v;
         }
       }
   }
 }
 
 // ================================================================ attention
-constexpr int kQBlk = 128;    // queries per workgroup, 32 per wave
-constexpr int kKTok = 64;     // keys per tile
-constexpr int kAttBuf = 3;    // tile buffers: one being read, two in flight
+constexpr int kAttWaves = 8;
+constexpr int kQBlk = 32 * kAttWaves;   // queries per workgroup, 32 per wave
+constexpr int kKTok = 64;               // keys per tile
+constexpr int kAttBuf = 3;              // tile buffers: one being read, two in flight
 
 template <int DN, int DV>
 struct AttnDims {
@@ -238,12 +263,14 @@ struct AttnDims {
   static constexpr int kVB = DV / 32;
   static constexpr int kFragV = kVB * 4;           // value fragments per tile (four 16-token k-steps)
   static constexpr int kFrag = kFragK + kFragV;
-  static_assert(kFrag % 4 == 0, "fragments must split evenly over four waves");
-  static constexpr int kDma = kFrag / 4;
+  static_assert(kFrag % kAttWaves == 0, "fragments must split evenly over the waves");
+  static constexpr int kDma = kFrag / kAttWaves;
 };
 
+// Two waves share each SIMD: while one runs its softmax (vector ALU, as much
+// work as the matrix products at these head widths) the other's products run.
 template <int DN, int DV>
-__global__ __launch_bounds__(256, 1) void extend_attn_kernel(
+__global__ __launch_bounds__(512, 1) void extend_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kexp, const bf16* __restrict__ vexp,
     const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
@@ -288,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void extend_attn_kernel(
       const int tb = f / Dm::kQS, s = f % Dm::kQS;
       if (16 * s < DN) {
         kind[u] = 0;
-        voff[u] = (uint32_t)(((32 * tb + l32) * DN + 16 * s + 8 * hh) * 2);
+        voff[u] = (uint32_t)((((tb * (DN / 16) + s) * 64) + lane) * 16);
       } else {
         kind[u] = 1;
         voff[u] = (uint32_t)(((32 * tb + l32) * kD + kDC + 16 * s - DN + 8 * hh) * 2);
@@ -296,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void extend_attn_kernel(
     } else {
       const int g = f - Dm::kFragK, vb = g / 4, s2 = g % 4;
       kind[u] = 2;
-      voff[u] = (uint32_t)(((32 * vb + l32) * kKTok + 16 * s2 + 8 * hh) * 2);
+      voff[u] = (uint32_t)((((vb * 4 + s2) * 64) + lane) * 16);
     }
   }
   const uint32_t lds0 = lds_address(&tiles[0][0]);
@@ -317,7 +344,9 @@ __global__ __launch_bounds__(256, 1) void extend_attn_kernel(
   };
 
   // ---- queries: B operand of k-step s holds dims 16 s + 8 hh .. + 7; the
-  // position part is rotated at the query's own position
+  // position part is rotated at the query's own position, and the whole
+  // query is multiplied by scale * log2(e) before rounding, so the scores
+  // come out in log2 units
   bf16x8 qf[Dm::kQS];
   {
     const bf16* src = q + ((int64_t)(q0 + qi) * H + h) * DQ + 8 * hh;
@@ -331,9 +360,12 @@ __global__ __launch_bounds__(256, 1) void extend_attn_kernel(
           float c, sn;
           rope_cos_sin_reduced(pos, freq.theta[pair], &c, &sn);
           const float x0 = to_f32(v[2 * m]), x1 = to_f32(v[2 * m + 1]);
-          v[2 * m] = from_f32<bf16>(x0 * c - x1 * sn);
-          v[2 * m + 1] = from_f32<bf16>(x0 * sn + x1 * c);
+          v[2 * m] = from_f32<bf16>((x0 * c - x1 * sn) * scale_log2e);
+          v[2 * m + 1] = from_f32<bf16>((x0 * sn + x1 * c) * scale_log2e);
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = from_f32<bf16>(to_f32(v[e]) * scale_log2e);
       }
       qf[s] = v;
     }
@@ -368,16 +400,18 @@ __global__ __launch_bounds__(256, 1) void extend_attn_kernel(
     // running max moves only when a score passes it by kRescaleThreshold
     const int tok0 = kt * kKTok;
     const bool masked = tok0 + kKTok - 1 > pos0 + i0;
+    if (masked) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (tok0 + 32 * tb + acc_row32(r, lane) > pos) S[tb][r] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = S[tb][r] * scale_log2e;
-        if (masked && tok0 + 32 * tb + acc_row32(r, lane) > pos) x = -INFINITY;
-        S[tb][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int r = 0; r < 16; r += 2) tmax = max_raw(tmax, max_raw(S[tb][r], S[tb][r + 1]));
     {
       const float2 hv = lane_halves(tmax);
       tmax = fmaxf(hv.x, hv.y);
@@ -433,7 +467,7 @@ void expand_for(const void* cache, const int32_t* seq_lens, const int32_t* page_
                 int batch, int H, int page_size, int lmax, const void* wukt, const void* wuv,
                 void* kexp, void* vexp, hipStream_t st) {
   const int nblocks = batch * H * (lmax / kExpTok);
-  expand_kv_kernel<DN, DV><<<nblocks, 256, 0, st>>>(
+  expand_kv_kernel<DN, DV><<<nblocks, 64 * kExpWaves, 0, st>>>(
       (const bf16*)cache, seq_lens, page_table, max_pages, batch, H, page_size, lmax,
       (const bf16*)wukt, (const bf16*)wuv, (bf16*)kexp, (bf16*)vexp);
 }
@@ -445,7 +479,7 @@ void attn_for(const void* q, const void* kexp, const void* vexp, const void* cac
               const RopeFreq& freq, float scale_log2e, void* out, hipStream_t st) {
   const int nqb = (max_q_len + kQBlk - 1) / kQBlk;
   const int nblocks = batch * H * nqb;
-  extend_attn_kernel<DN, DV><<<nblocks, 256, 0, st>>>(
+  extend_attn_kernel<DN, DV><<<nblocks, 64 * kAttWaves, 0, st>>>(
       (const bf16*)q, (const bf16*)kexp, (const bf16*)vexp, (const bf16*)cache, cu_q, seq_lens,
       page_table, max_pages, batch, H, page_size, lmax, nqb, freq, scale_log2e, (bf16*)out);
 }

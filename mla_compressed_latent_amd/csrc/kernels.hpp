@@ -71,12 +71,16 @@ void launch_combine(int elem, const SplitPlan& plan, const float* opart, const f
 // Whether the expanded kernels are built for these head widths.
 bool extend_expanded_supported(int dn, int dv);
 // Per head, materialise the content keys and the values of every cached token
-// of every sequence from its latent row:
-//   kexp[b][h][t][i]                  = sum_j c_t[j] W_uk[j][h*dn + i]
-//   vexp[b][h][t/64][v][perm(t % 64)] = sum_j c_t[j] W_uv[j][h*dv + v]
-// for t < round_up(seq_len_b, 128) (rows past seq_len_b repeat the last row);
-// perm swaps bits 2 and 3 of the token index inside each group of 16.
-// lmax (a multiple of 128) is the token stride of one (sequence, head).
+// of every sequence from its latent row, K_h[t][i] = sum_j c_t[j] W_uk[j][h*dn+i]
+// and V_h[t][v] = sum_j c_t[j] W_uv[j][h*dv+v], for t < round_up(seq_len_b,
+// 256) (rows past seq_len_b repeat the last row).  Both are stored per
+// (sequence, head, 64-token tile) as 1 KB matrix-core operand fragments
+// (64 lanes x 8 bf16):
+//   kexp: fragment (tb, s), tb < 2, s < dn/16: lane l holds K[32 tb + l%32]
+//         [16 s + 8 (l/32) .. + 7];
+//   vexp: fragment (vb, k), vb < dv/32, k < 4: lane l holds V[t][32 vb + l%32]
+//         for the eight tokens t = 16 k + 8 (e/4) + 4 (l/32) + e%4, e = 0..7.
+// lmax (a multiple of 256) is the token stride of one (sequence, head).
 void launch_expand_kv(const void* cache, const int32_t* seq_lens, const int32_t* page_table,
                       int max_pages, int batch, int H, int dn, int dv, int page_size, int lmax,
                       const void* wukt, const void* wuv, void* kexp, void* vexp, hipStream_t st);
