@@ -96,7 +96,18 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
 
     cfg = mla.config_from_shape(s)
     w_dkv, w_uk, w_uv = up(wl.w_dkv()), up(wl.w_uk()), up(wl.w_uv())
-    table_np, num_pages = wl.page_table()
+    pool = None
+    if wl.layers:
+        # a layer stack: one host page pool assigns every sequence's pages, and
+        # its table serves all layers' caches
+        npg = wl.pages_per_seq()
+        num_pages = int(npg.sum())
+        pool = mla.PagePool(num_pages, s.page_size, wl.batch, int(npg.max()))
+        for b, L in enumerate(wl.seq_lens()):
+            pool.reserve(b, int(L))
+        table_np = pool.page_table(list(range(wl.batch)))
+    else:
+        table_np, num_pages = wl.page_table()
     table = i32(table_np)
     prefix = wl.prefix_lens()
     q_lens = wl.q_lens()
@@ -138,7 +149,7 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
 
     cache_bytes = cache0.numel() * cache0.element_size()
     folded_bytes = layer0.folded.numel()
-    R = rotate or max(1, math.ceil((1 << 30) / (cache_bytes + folded_bytes)))
+    R = wl.layers or rotate or max(1, math.ceil((1 << 30) / (cache_bytes + folded_bytes)))
     layers, caches = [layer0], [cache0]
     for _ in range(R - 1):
         layers.append(mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv))
@@ -153,7 +164,7 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
         seq_lens=i32(seq_lens_np), seq_lens_np=seq_lens_np, max_q_len=int(q_lens.max()),
         max_seq_len=int(seq_lens_np.max()), kv_chunk=kv_chunk,
         out=torch.empty((Tq, s.H, s.d_v), dtype=dt, device=dev),
-        cache_bytes=cache_bytes, folded_bytes=folded_bytes,
+        cache_bytes=cache_bytes, folded_bytes=folded_bytes, cfg=cfg, pool=pool,
     )
     st["chunk"] = mla.mla_decode_kv_chunk(layer0, B, st["max_q_len"], st["max_seq_len"], kv_chunk)
     st["aws"] = torch.empty(max(1, mla.mla_append_workspace_bytes(layer0, Tq)), dtype=torch.uint8, device=dev)
@@ -441,6 +452,20 @@ def main():
     res["hardware"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                        "compute_units": props.multi_processor_count,
                        "memory_GB": round(props.total_memory / 1e9, 1)}
+    if wl.layers:
+        # one graph replay is one decode forward through every layer
+        mla = st["mla"]
+        fwd_ms = ms_step * wl.layers
+        weights = st["folded_bytes"] * wl.layers
+        res["stack"] = {
+            "layers": wl.layers, "forward_ms": fwd_ms, "forward_tokens_per_s": wl.batch / (fwd_ms * 1e-3),
+            "cache_GB": st["cache_bytes"] * wl.layers / 1e9, "folded_weights_GB": weights / 1e9,
+            "page_table": "host page pool (mla_pool_*), one table for all layers",
+            # sequences of this context the planner fits in the device memory left
+            # after the folded weights (cache alone, as the capacity argument counts it)
+            "planner_max_sequences": mla.mla_plan_max_sequences(
+                st["cfg"], wl.layers, int(props.total_memory - weights), st["max_seq_len"]),
+        }
     print(json.dumps(res), flush=True)
 
 

@@ -256,6 +256,74 @@ mla_status mla_extend(const mla_layer* layer, const void* q, const int32_t* cu_q
                       int32_t path, const void* cache, int64_t num_pages, void* out,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * A stack of layers: capacity planning and one page pool for every layer.
+ * ("Multi-head Latent Attention: the KV cache, compressed", sections "The
+ * one formula": a token costs num_layers * (d_c + d_rope) elements of cache
+ * whatever the head count; "Where the saving actually lands": what matters
+ * is how many whole sequences of a context fit one cache budget.)
+ *
+ * Every layer holds the same tokens of the same sequences, so one page table
+ * serves all layers: each layer has its own cache tensor
+ * [num_pages][page_size][d_c + d_rope] (for example slice l of one
+ * [num_layers][num_pages][...] allocation), and page p of a sequence is page
+ * p of every layer's tensor.  Host-only calls: nothing here touches the GPU.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_layers;
+  int32_t page_size;
+  int64_t num_pages;        /* pages of each layer's cache                   */
+  size_t page_bytes;        /* one page of one layer: page_size * row bytes  */
+  size_t layer_bytes;       /* num_pages * page_bytes                        */
+  size_t total_bytes;       /* num_layers * layer_bytes, <= the budget       */
+  size_t bytes_per_token;   /* num_layers * (d_c + d_rope) * dtype bytes     */
+} mla_cache_plan;
+
+/* The most whole pages (the same count in every layer, at most 2^31 - 1)
+ * whose caches fit budget_bytes.  Errors: INVALID_ARG (bad cfg, num_layers
+ * < 1, out null), INSUFFICIENT_WORKSPACE (not one page of every layer fits). */
+mla_status mla_plan_cache(const mla_config* cfg, int32_t num_layers, size_t budget_bytes,
+                          mla_cache_plan* out);
+
+/* Whole sequences of `context` tokens that budget_bytes holds across
+ * num_layers layers, each taking ceil(context / page_size) pages of every
+ * layer: floor(budget / (num_layers * pages * page_bytes)).  -1 on invalid
+ * arguments. */
+int64_t mla_plan_max_sequences(const mla_config* cfg, int32_t num_layers, size_t budget_bytes,
+                               int64_t context);
+
+typedef struct mla_page_pool mla_page_pool; /* opaque host allocator */
+
+/* An allocator of num_pages pages (page ids 0 .. num_pages-1, shared by all
+ * layers) for sequence ids 0 .. max_seqs-1 of up to max_pages_per_seq pages
+ * each.  A fresh pool hands pages out in ascending order; released pages are
+ * handed out again first, the most recently released first, each sequence's
+ * pages in their old order.  Not thread safe.  Errors: INVALID_ARG. */
+mla_status mla_pool_create(int64_t num_pages, int32_t page_size, int32_t max_seqs,
+                           int32_t max_pages_per_seq, mla_page_pool** out);
+void mla_pool_destroy(mla_page_pool* pool);
+
+/* Grow sequence `seq` to hold `length` tokens: pages are added at its end,
+ * never removed or moved (rows already cached stay where they are).
+ * INVALID_ARG for a bad id or a length beyond max_pages_per_seq * page_size;
+ * INSUFFICIENT_WORKSPACE when the free pages do not cover the growth (the
+ * pool is then unchanged). */
+mla_status mla_pool_reserve(mla_page_pool* pool, int32_t seq, int64_t length);
+
+/* Return every page of `seq` to the pool; its reserved length becomes 0. */
+mla_status mla_pool_release(mla_page_pool* pool, int32_t seq);
+
+/* Free pages, and the tokens reserved for `seq` (-1 on bad arguments). */
+int64_t mla_pool_free_pages(const mla_page_pool* pool);
+int64_t mla_pool_length(const mla_page_pool* pool, int32_t seq);
+
+/* The page-table rows of n sequences, ready to copy to the device for
+ * mla_append_latent / mla_decode / mla_extend of any layer: table is a HOST
+ * buffer [n][max_pages_per_seq] int32, row i = the pages of seqs[i] in token
+ * order, then -1.  Errors: INVALID_ARG. */
+mla_status mla_pool_page_table(const mla_page_pool* pool, const int32_t* seqs, int32_t n,
+                               int32_t* table);
+
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 

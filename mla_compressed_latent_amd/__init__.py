@@ -22,6 +22,7 @@ __all__ = [
     "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
     "MLA_PHASE_ALL", "mla_extend_choose_path", "mla_extend_workspace_bytes", "mla_extend",
     "MLA_EXTEND_AUTO", "MLA_EXTEND_ABSORBED", "MLA_EXTEND_EXPANDED",
+    "MlaCachePlan", "mla_plan_cache", "mla_plan_max_sequences", "PagePool",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -35,7 +36,9 @@ EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
     "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_extend_choose_path",
-    "mla_extend_workspace_bytes", "mla_extend", "mla_status_string", "mla_last_error",
+    "mla_extend_workspace_bytes", "mla_extend", "mla_plan_cache", "mla_plan_max_sequences",
+    "mla_pool_create", "mla_pool_destroy", "mla_pool_reserve", "mla_pool_release", "mla_pool_free_pages",
+    "mla_pool_length", "mla_pool_page_table", "mla_status_string", "mla_last_error",
 )
 
 
@@ -64,6 +67,18 @@ class MlaConfig(ctypes.Structure):
         return torch.bfloat16 if self.dtype == MLA_DTYPE_BF16 else torch.float32
 
 
+class MlaCachePlan(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("page_bytes", ctypes.c_size_t),
+        ("layer_bytes", ctypes.c_size_t),
+        ("total_bytes", ctypes.c_size_t),
+        ("bytes_per_token", ctypes.c_size_t),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -87,6 +102,15 @@ def _load():
         "mla_extend_choose_path": (I32, [cfgp, I32, I32, I32, I32]),
         "mla_extend_workspace_bytes": (S, [P, I32, I32, I32, I32, I32]),
         "mla_extend": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
+        "mla_plan_cache": (I32, [cfgp, I32, S, ctypes.POINTER(MlaCachePlan)]),
+        "mla_plan_max_sequences": (I64, [cfgp, I32, S, I64]),
+        "mla_pool_create": (I32, [I64, I32, I32, I32, ctypes.POINTER(P)]),
+        "mla_pool_destroy": (None, [P]),
+        "mla_pool_reserve": (I32, [P, I32, I64]),
+        "mla_pool_release": (I32, [P, I32]),
+        "mla_pool_free_pages": (I64, [P]),
+        "mla_pool_length": (I64, [P, I32]),
+        "mla_pool_page_table": (I32, [P, P, I32, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
@@ -283,3 +307,53 @@ def mla_extend(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_le
         int(max_seq_len), int(path), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
         "mla_extend")
+
+
+def mla_plan_cache(cfg: MlaConfig, num_layers: int, budget_bytes: int) -> MlaCachePlan:
+    plan = MlaCachePlan()
+    _check(lib.mla_plan_cache(ctypes.byref(cfg), int(num_layers), int(budget_bytes), ctypes.byref(plan)),
+           "mla_plan_cache")
+    return plan
+
+
+def mla_plan_max_sequences(cfg: MlaConfig, num_layers: int, budget_bytes: int, context: int) -> int:
+    return int(lib.mla_plan_max_sequences(ctypes.byref(cfg), int(num_layers), int(budget_bytes), int(context)))
+
+
+class PagePool:
+    """Host page allocator shared by every layer's cache (mla_pool_*)."""
+
+    def __init__(self, num_pages: int, page_size: int, max_seqs: int, max_pages_per_seq: int):
+        h = ctypes.c_void_p()
+        _check(lib.mla_pool_create(int(num_pages), int(page_size), int(max_seqs), int(max_pages_per_seq),
+                                   ctypes.byref(h)), "mla_pool_create")
+        self.handle = h
+        self.max_pages_per_seq = int(max_pages_per_seq)
+        self._destroy = lib.mla_pool_destroy   # still bound at interpreter exit
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            self._destroy(h)
+            self.handle = None
+
+    def reserve(self, seq: int, length: int):
+        _check(lib.mla_pool_reserve(self.handle, int(seq), int(length)), "mla_pool_reserve")
+
+    def release(self, seq: int):
+        _check(lib.mla_pool_release(self.handle, int(seq)), "mla_pool_release")
+
+    def free_pages(self) -> int:
+        return int(lib.mla_pool_free_pages(self.handle))
+
+    def length(self, seq: int) -> int:
+        return int(lib.mla_pool_length(self.handle, int(seq)))
+
+    def page_table(self, seqs):
+        """int32 host array [len(seqs)][max_pages_per_seq]."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        out = np.empty((ids.shape[0], self.max_pages_per_seq), dtype=np.int32)
+        _check(lib.mla_pool_page_table(self.handle, ids.ctypes.data_as(ctypes.c_void_p), int(ids.shape[0]),
+                                       out.ctypes.data_as(ctypes.c_void_p)), "mla_pool_page_table")
+        return out

@@ -198,6 +198,15 @@ int choose_extend_path(const mla_config& c, int batch, int total_q, int max_q_le
 
 }  // namespace
 
+// Shared with the host-only parts of the library (pool.cpp).
+namespace mla_api {
+mla_status fail_msg(mla_status s, const char* msg) { return fail(s, "%s", msg); }
+size_t row_bytes(const mla_config* cfg) {
+  if (check_config(cfg) != MLA_OK) return 0;
+  return (size_t)(cfg->kv_lora_rank + cfg->qk_rope_head_dim) * elem_of(cfg);
+}
+}  // namespace mla_api
+
 #pragma GCC visibility push(default)
 extern "C" {
 

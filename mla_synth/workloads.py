@@ -127,6 +127,8 @@ class Workload:
     description: str = ""
     kind: str = "decode"              # "decode": the step is append + mla_decode;
                                       # "extend": append + mla_extend (long chunks)
+    layers: int = 0                   # > 0: a stack of this many layers sharing one
+                                      # page-pool table (one timed pass = all layers)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -257,6 +259,11 @@ WORKLOADS = {
         fixed_prefix=None, max_prefix=32768, fixed_q_len=None, max_q_len=2, spare_page_frac=0.05,
         description="bf16; DeepSeek-V2 shape, 256 sequences, prefix ~ U[1, 32768], q_len ~ U{1,2}, "
                     "64-token pages under a random page table, new tokens appended first"),
+    "dsv2_60layers_b32_ctx4096": Workload(
+        "dsv2_60layers_b32_ctx4096", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
+        layers=60,
+        description="bf16; DeepSeek-V2 shape, all 60 layers (one page-pool table), batch 32, "
+                    "every context 4096, q_len 1"),
     "dsv2_extend_b4_p3072_c1024": Workload(
         "dsv2_extend_b4_p3072_c1024", DSV2, batch=4, seed=6, prefix_source="hidden", fixed_prefix=3072,
         fixed_q_len=1024, max_q_len=1024, kind="extend",
