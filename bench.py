@@ -37,13 +37,33 @@ EXTEND_METRIC = "MLA chunked-extend / prefill query tokens/s and matrix-core TFL
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("ca6764d795ac493c", "dsv2_b32_ctx4096"): {"fetch_bytes": 155910612, "write_bytes": 35831633},
-    ("ca6764d795ac493c", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606557504, "write_bytes": 16811723},
-    ("ca6764d795ac493c", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210457128, "write_bytes": 72269077},
+    ("0f5bc7de432501f4", "dsv2_b32_ctx4096"): {"fetch_bytes": 155908688, "write_bytes": 37031179},
+    ("0f5bc7de432501f4", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606557382, "write_bytes": 16810543},
+    ("0f5bc7de432501f4", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210452377, "write_bytes": 73165852},
 }
 
 
 ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip")
+
+
+EXTEND_SOURCES = ("attn_tile.hpp", "extend.hip")
+# HBM bytes of one mla_extend call (both expanded kernels), measured as above.
+EXTEND_TRAFFIC = {
+    ("e2bea4fc8d28dd01", "dsv2_extend_b4_p3072_c1024"): {
+        "fetch_bytes": 2519772697, "write_bytes": 1207990337,
+        "per_kernel": {"expand_kv": {"fetch_bytes": 1207949201, "write_bytes": 1073741824},
+                       "extend_attn": {"fetch_bytes": 1311823497, "write_bytes": 134248513}}},
+}
+
+
+def extend_source_id():
+    """Hash of the expanded extend kernels' sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in EXTEND_SOURCES:
+        with open(os.path.join(ROOT, "mla_compressed_latent_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def splitkv_source_id():
@@ -550,7 +570,11 @@ def main_extend(args, wl, st):
         "extend_ms_by_path": path_ms,
         "roofline": {
             "bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": (None if not expanded or (extend_source_id(), wl.name) not in EXTEND_TRAFFIC else
+                        EXTEND_TRAFFIC[(extend_source_id(), wl.name)]["fetch_bytes"] +
+                        EXTEND_TRAFFIC[(extend_source_id(), wl.name)]["write_bytes"]),
+            "traffic_detail": EXTEND_TRAFFIC.get((extend_source_id(), wl.name)) if expanded else None,
             "kernel": f"mla_extend ({names[st['path']]}: both of its kernels, HIP events around the call)",
             "algorithmic_flops_per_launch": f_side + f_attn,
             "flops_split": {"expand_or_fold": f_side, "attention": f_attn},
