@@ -133,7 +133,10 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
     q_lens = wl.q_lens()
     seq_lens_np = wl.seq_lens()
     B = wl.batch
-    cache0 = torch.empty((num_pages, s.page_size, s.row_width), dtype=dt, device=dev)
+    if s.cache_format == "fp8":   # pages of 640-byte rows, then the rows' fp32 scales
+        cache0 = torch.empty((num_pages, s.page_size * s.cache_token_bytes), dtype=torch.uint8, device=dev)
+    else:
+        cache0 = torch.empty((num_pages, s.page_size, s.row_width), dtype=dt, device=dev)
     layer0 = mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv)
 
     t0 = time.time()
@@ -152,6 +155,7 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
                 torch.cuda.synchronize()
                 del x, xs
         else:
+            assert s.cache_format != "fp8", "fp8 caches are filled through the append path"
             futs = {b: ex.submit(wl.prefix_latent, b) for b in range(min(B, 16))}
             for b in range(B):
                 if b + 16 < B:
@@ -263,7 +267,7 @@ def cpu_baseline(wl, budget_s):
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
-    from oracle import mla_oracle
+    from oracle import fp8, mla_oracle
 
     s = wl.shape
     w_dkv, w_uk, w_uv = wl.w_dkv(), wl.w_uk(), wl.w_uv()
@@ -285,6 +289,8 @@ def cpu_baseline(wl, budget_s):
             t0 = time.perf_counter()
             new = mla_oracle.latent_rows(x_new, w_dkv, P + np.arange(x_new.shape[0]), s.d_c, s.rope_base)
             cache = np.concatenate([pre, new], axis=0)
+            if s.cache_format == "fp8":
+                cache = fp8.fp8_rows(cache, s.d_c)
             mla_oracle.attend_sequence(q, cache, w_uk, w_uv, s.H, s.d_nope, s.d_v, s.rope_base, scale)
             elapsed += time.perf_counter() - t0
             done_q += q.shape[0]
@@ -416,7 +422,7 @@ def main():
     torch.cuda.synchronize()
     warm_ms_step = w0.elapsed_time(w1) / (max(1, K // R) * R)
     s = st["s"]
-    latent_bytes = int(st["seq_lens_np"].astype("int64").sum()) * s.row_width * (2 if s.dtype == "bf16" else 4)
+    latent_bytes = int(st["seq_lens_np"].astype("int64").sum()) * s.cache_token_bytes
     attend_s = phase[2] * 1e-3
     achieved = latent_bytes / attend_s / 1e9
     # scores (K = d_c + d_rope) and value sums (K = d_c) per query row and cached token

@@ -67,6 +67,23 @@ typedef enum {
 
 typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
 
+/* How cache pages store their rows.
+ *   MLA_CACHE_DTYPE   rows [c | k_rope] in the layer dtype; a page is
+ *                     [page_size][d_c + d_rope] elements.
+ *   MLA_CACHE_FP8     (bf16 layers) the latent c of each row is quantized
+ *                     to 8-bit floats, OCP E4M3 (1 sign, 4 exponent bits of
+ *                     bias 7, 3 mantissa bits, no infinities, largest finite
+ *                     448), with one power-of-two scale per row: c ~= 2^e *
+ *                     code, e the smallest integer with max|c| <= 448 * 2^e
+ *                     (0 for an all-zero latent), codes rounded to nearest
+ *                     even.  The rotated rope key stays bf16.  A page is
+ *                     page_size rows of 640 bytes (512 codes, then 64 bf16),
+ *                     then page_size fp32 scales 2^e: page_size * 644 bytes.
+ *                     ("Moving a trained MHA model over" on the "Multi-head
+ *                     Latent Attention and KV Cache Compression" page: the
+ *                     latent can be quantized further, with scales.) */
+typedef enum { MLA_CACHE_DTYPE = 0, MLA_CACHE_FP8 = 1 } mla_cache_format;
+
 /* Shape of one MLA layer.  Field names follow the Hugging Face DeepSeek-V2
  * config.  bf16 layers need kv_lora_rank == 512, qk_rope_head_dim == 64,
  * qk_nope_head_dim (at most 256) and v_head_dim multiples of 32 and d_model a
@@ -84,6 +101,7 @@ typedef struct {
   float rope_base;              /* rotary base, e.g. 10000                     */
   float softmax_scale;          /* <= 0 selects 1/sqrt(d_nope + d_rope)         */
   mla_dtype dtype;              /* storage dtype of every tensor               */
+  int32_t cache_format;         /* an mla_cache_format (0: rows in dtype)       */
 } mla_config;
 
 typedef struct mla_layer mla_layer; /* opaque host handle */
@@ -114,7 +132,9 @@ void mla_layer_free(mla_layer* layer);
 
 /* Bytes one token occupies in the cache: (d_c + d_rope) * sizeof(dtype)
  * ("The one formula": one latent plus one position key per token and layer,
- * independent of the head count).  0 if cfg is invalid. */
+ * independent of the head count); 644 for MLA_CACHE_FP8 (512 codes, 128
+ * bytes of rope key, a 4-byte scale).  A page holds page_size times this.
+ * 0 if cfg is invalid. */
 size_t mla_cache_bytes_per_token(const mla_config* cfg);
 
 /* Workspace mla_append_latent needs for total_new new tokens. */
@@ -215,8 +235,8 @@ mla_status mla_decode_phases(const mla_layer* layer, const void* q, const int32_
  *                        c W_uv_h are built once per cached token into the
  *                        workspace, then causal flash attention runs at width
  *                        d_nope + d_rope (scores) and d_v (values).  bf16
- *                        layers with qk_nope_head_dim and v_head_dim each 64
- *                        or 128;
+ *                        layers with a bf16 cache (MLA_CACHE_DTYPE) and
+ *                        qk_nope_head_dim and v_head_dim each 64 or 128;
  *   MLA_EXTEND_AUTO      the form with less matrix-core work for these
  *                        bounds (see mla_extend_choose_path). */
 typedef enum {

@@ -22,7 +22,7 @@ __all__ = [
     "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
     "MLA_PHASE_ALL", "mla_extend_choose_path", "mla_extend_workspace_bytes", "mla_extend",
     "MLA_EXTEND_AUTO", "MLA_EXTEND_ABSORBED", "MLA_EXTEND_EXPANDED",
-    "MlaCachePlan", "mla_plan_cache", "mla_plan_max_sequences", "PagePool",
+    "MlaCachePlan", "mla_plan_cache", "mla_plan_max_sequences", "PagePool", "MLA_CACHE_DTYPE", "MLA_CACHE_FP8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -31,6 +31,7 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_INSUFFICI
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 MLA_PHASE_ABSORB, MLA_PHASE_ATTEND, MLA_PHASE_OUTPUT, MLA_PHASE_ALL = 1, 2, 4, 7
 MLA_EXTEND_AUTO, MLA_EXTEND_ABSORBED, MLA_EXTEND_EXPANDED = 0, 1, 2
+MLA_CACHE_DTYPE, MLA_CACHE_FP8 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
@@ -60,11 +61,17 @@ class MlaConfig(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("cache_format", ctypes.c_int32),
     ]
 
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == MLA_DTYPE_BF16 else torch.float32
+
+    @property
+    def cache_torch_dtype(self):
+        """Element type of cache tensors: the layer dtype, or bytes for FP8 pages."""
+        return torch.uint8 if self.cache_format == MLA_CACHE_FP8 else self.torch_dtype
 
 
 class MlaCachePlan(ctypes.Structure):
@@ -162,7 +169,8 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> ctypes.c_void_p:
 
 
 def config_from_shape(shape, softmax_scale: float = 0.0) -> MlaConfig:
-    """MlaConfig from an object with the Hugging Face field names."""
+    """MlaConfig from an object with the Hugging Face field names (and an
+    optional ``cache_format``: "dtype" or "fp8")."""
     return MlaConfig(
         d_model=shape.d_model,
         num_attention_heads=shape.num_attention_heads,
@@ -174,6 +182,7 @@ def config_from_shape(shape, softmax_scale: float = 0.0) -> MlaConfig:
         rope_base=float(shape.rope_base),
         softmax_scale=float(softmax_scale),
         dtype=MLA_DTYPE_BF16 if shape.dtype == "bf16" else MLA_DTYPE_F32,
+        cache_format=MLA_CACHE_FP8 if getattr(shape, "cache_format", "dtype") == "fp8" else MLA_CACHE_DTYPE,
     )
 
 
@@ -238,7 +247,7 @@ def mla_append_latent(layer: Layer, x, cu_new, prefix_lens, page_table, cache, w
     _check(lib.mla_append_latent(
         layer.handle, _dev(x, "x", dt), _dev(cu_new, "cu_new", torch.int32),
         _dev(prefix_lens, "prefix_lens", torch.int32), _dev(page_table, "page_table", torch.int32),
-        int(page_table.shape[1]), batch, total_new, _dev(cache, "cache", dt), int(cache.shape[0]),
+        int(page_table.shape[1]), batch, total_new, _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
         "mla_append_latent")
 
@@ -274,7 +283,7 @@ def mla_decode_phases(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, m
     _check(lib.mla_decode_phases(
         layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
         _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
-        int(max_seq_len), int(kv_chunk), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
+        int(max_seq_len), int(kv_chunk), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
         int(phases)), "mla_decode")
 
@@ -304,7 +313,7 @@ def mla_extend(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_le
     _check(lib.mla_extend(
         layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
         _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
-        int(max_seq_len), int(path), _dev(cache, "cache", dt), int(cache.shape[0]), _dev(out, "out", dt),
+        int(max_seq_len), int(path), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
         "mla_extend")
 

@@ -67,7 +67,17 @@ mla_status check_config(const mla_config* c) {
   } else {
     return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
   }
+  if (c->cache_format != MLA_CACHE_DTYPE && c->cache_format != MLA_CACHE_FP8)
+    return fail(MLA_ERR_INVALID_ARG, "unknown cache_format %d", (int)c->cache_format);
+  if (c->cache_format == MLA_CACHE_FP8 && c->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "the FP8 cache format needs a bf16 layer");
   return MLA_OK;
+}
+
+// Bytes of one cached token (row plus, for FP8, its scale).
+size_t token_bytes(const mla_config* c) {
+  if (c->cache_format == MLA_CACHE_FP8) return mla::kFp8RowBytes + 4;
+  return (size_t)(c->kv_lora_rank + c->qk_rope_head_dim) * (c->dtype == MLA_DTYPE_BF16 ? 2 : 4);
 }
 
 int elem_of(const mla_config* c) { return c->dtype == MLA_DTYPE_BF16 ? 2 : 4; }
@@ -172,7 +182,8 @@ ExtendLayout extend_layout(const mla_config& c, int batch, int max_seq_len) {
 }
 
 bool expanded_available(const mla_config& c) {
-  return c.dtype == MLA_DTYPE_BF16 && mla::extend_expanded_supported(c.qk_nope_head_dim, c.v_head_dim);
+  return c.dtype == MLA_DTYPE_BF16 && c.cache_format == MLA_CACHE_DTYPE &&
+         mla::extend_expanded_supported(c.qk_nope_head_dim, c.v_head_dim);
 }
 
 // Matrix-core work of the two forms for these host bounds (average keys per
@@ -203,7 +214,7 @@ namespace mla_api {
 mla_status fail_msg(mla_status s, const char* msg) { return fail(s, "%s", msg); }
 size_t row_bytes(const mla_config* cfg) {
   if (check_config(cfg) != MLA_OK) return 0;
-  return (size_t)(cfg->kv_lora_rank + cfg->qk_rope_head_dim) * elem_of(cfg);
+  return token_bytes(cfg);
 }
 }  // namespace mla_api
 
@@ -230,7 +241,7 @@ size_t mla_folded_bytes(const mla_config* cfg) {
 
 size_t mla_cache_bytes_per_token(const mla_config* cfg) {
   if (check_config(cfg) != MLA_OK) return 0;
-  return (size_t)(cfg->kv_lora_rank + cfg->qk_rope_head_dim) * elem_of(cfg);
+  return token_bytes(cfg);
 }
 
 mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void* w_uk,
@@ -309,9 +320,13 @@ mla_status mla_append_latent(const mla_layer* L, const void* x, const int32_t* c
   } else {
     mla::launch_append_gemm_f32(x, L->wdkv_t, part, total_new, D, c.d_model, st);
   }
-  mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
-                            batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
-                            L->freq, st);
+  if (c.cache_format == MLA_CACHE_FP8)
+    mla::launch_append_finish_fp8(part, ks, total_new, cu_new, prefix_lens, page_table, max_pages, batch,
+                                  cache, c.page_size, L->freq, st);
+  else
+    mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
+                              batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
+                              L->freq, st);
   return hip_check("append launch");
 }
 
@@ -374,7 +389,8 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
                        L->scale * 1.4426950408889634f, st);
   if (phases & MLA_PHASE_ATTEND)
     mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
-                        c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse, st);
+                        c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
+                        c.cache_format == MLA_CACHE_FP8, st);
   if (phases & MLA_PHASE_OUTPUT) {
     if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
       mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
@@ -443,8 +459,8 @@ mla_status mla_extend(const mla_layer* L, const void* q, const int32_t* cu_q, co
   const mla_config& c = L->cfg;
   if (!expanded_available(c))
     return fail(MLA_ERR_UNSUPPORTED,
-                "mla_extend: the expanded path needs a bf16 layer with qk_nope_head_dim and v_head_dim "
-                "each 64 or 128");
+                "mla_extend: the expanded path needs a bf16 layer with a bf16 cache and "
+                "qk_nope_head_dim and v_head_dim each 64 or 128");
   const ExtendLayout e = extend_layout(c, batch, max_seq_len);
   if (workspace_bytes < e.total)
     return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "extend workspace holds %zu bytes, %zu needed",

@@ -68,6 +68,102 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// ---- FP8 cache tiles (MLA_CACHE_FP8 pages: rows of 512 E4M3 codes and 64
+// bf16 of rope key, the page's fp32 row scales after its rows).  A tile's 32
+// rows and 32 scales are copied to a staging buffer, then converted once into
+// the bf16 tile layout above; with power-of-two scales the dequantized values
+// code * 2^e are exact in bf16, so the attention arithmetic that follows is
+// the bf16 path's.
+constexpr int kF8Row = 640;
+constexpr int kF8RowsBytes = kTileTok * kF8Row;       // 20480
+constexpr int kF8StageBytes = kF8RowsBytes + 1024;     // + one wave-wide copy holding the scales
+constexpr int kF8Dma = kF8RowsBytes / 1024 + 1;        // 21 wave-wide copies per tile
+
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+// All copies of one FP8 tile, issued by one wave: `page` is the page's first
+// byte, `tok_in_page` the tile's first row in it (tiles never cross pages).
+__device__ __forceinline__ void f8_issue(const uint8_t* page, int page_size, int tok_in_page,
+                                         uint32_t lds_stage, int lane) {
+  const uint8_t* rows = page + (size_t)tok_in_page * kF8Row;
+#pragma unroll
+  for (int u = 0; u < kF8RowsBytes / 1024; ++u)
+    dma16(rows, (uint32_t)((u * 64 + lane) * 16), lds_stage + u * 1024);
+  // 128 bytes of scales; lanes past the eighth repeat them (never read)
+  const uint8_t* sc = page + (size_t)page_size * kF8Row + (size_t)tok_in_page * 4;
+  dma16(sc, (uint32_t)((lane & 7) * 16), lds_stage + kF8RowsBytes);
+}
+
+// Items item0, item0 + istep, ... of one staged tile into the bf16 tile:
+// latent items 0..1023 (row i / 32, codes 16 (i % 32) .. + 15 -> bf16 chunks
+// 2 (i % 32) and + 1) and rope items 0..255 (row i / 8, chunk 64 + i % 8).
+// Rows at or past nvalid are written as zeros, so that zero probabilities
+// never meet whatever the page held there.  U items per lane go at a time:
+// all their staging reads first, so that the LDS latency is paid once per
+// batch rather than once per item.
+template <int U>
+__device__ __forceinline__ void f8_convert(const char* stage, char* tile, int nvalid, int item0,
+                                           int istep) {
+  const float* scales = reinterpret_cast<const float*>(stage + kF8RowsBytes);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 1
+  for (int base = item0; base < kTileTok * 32; base += U * istep) {
+    u32x4 w[U];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * istep, t = i >> 5;
+      w[u] = zero;
+      sc[u] = 0.f;
+      if (i < kTileTok * 32 && t < nvalid) {
+        w[u] = *reinterpret_cast<const u32x4*>(stage + t * kF8Row + (i & 31) * 16);
+        sc[u] = scales[t];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * istep, t = i >> 5, k = i & 31;
+      if (i >= kTileTok * 32) break;
+      u32x4 lo = zero, hi = zero;
+      if (t < nvalid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v2bf16 x = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[u][q], sc[u], false);
+          const v2bf16 y = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[u][q], sc[u], true);
+          const uint32_t ux = __builtin_bit_cast(uint32_t, x), uy = __builtin_bit_cast(uint32_t, y);
+          if (q < 2) {
+            lo[2 * q] = ux;
+            lo[2 * q + 1] = uy;
+          } else {
+            hi[2 * q - 4] = ux;
+            hi[2 * q - 3] = uy;
+          }
+        }
+      }
+      const int sw = swz(t);
+      *reinterpret_cast<u32x4*>(tile + (t * kChunks + ((2 * k) ^ sw)) * 16) = lo;
+      *reinterpret_cast<u32x4*>(tile + (t * kChunks + ((2 * k + 1) ^ sw)) * 16) = hi;
+    }
+  }
+#pragma unroll 1
+  for (int base = item0; base < kTileTok * 8; base += U * istep) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * istep, t = i >> 3;
+      w[u] = zero;
+      if (i < kTileTok * 8 && t < nvalid)
+        w[u] = *reinterpret_cast<const u32x4*>(stage + t * kF8Row + 512 + (i & 7) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * istep, t = i >> 3;
+      if (i >= kTileTok * 8) break;
+      *reinterpret_cast<u32x4*>(tile + (t * kChunks + 64 + ((i & 7) ^ swz(t))) * 16) = w[u];
+    }
+  }
+}
+
 // Score MFMAs with the accumulator in VGPRs.  The compiler keeps every other
 // matrix-core accumulator of this kernel (the 256 registers of O) in AGPRs;
 // issuing the score chain as assembly keeps its 16 accumulators out of that

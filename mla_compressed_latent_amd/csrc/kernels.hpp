@@ -8,6 +8,11 @@
 
 namespace mla {
 
+// FP8 cache pages (MLA_CACHE_FP8): page_size rows of kFp8RowBytes (512 E4M3
+// latent codes, then the 64 bf16 of the rotated rope key), then page_size
+// fp32 row scales.
+constexpr int kFp8RowBytes = 640;
+
 // ---- fold (pack) ---------------------------------------------------------
 // bf16 (elem 2): fragment-tiled wdkv (rows n, k = d), wuk[h] (rows j, k = i),
 // wuv[h] (rows v, k = j), wukt[h] (rows i, k = j).  fp32 (elem 4):
@@ -30,6 +35,13 @@ void launch_append_finish(int elem, const float* part, int ksplits, int T, const
                           int batch, void* cache, int page_size, int dc, int dr, float base,
                           const RopeFreq& freq, hipStream_t st);
 
+// FP8 cache rows (bf16 layers, d_c 512, d_rope 64): quantize each new row's
+// latent with its power-of-two scale, rotate and round its rope key.
+void launch_append_finish_fp8(const float* part, int ksplits, int T, const int32_t* cu_new,
+                              const int32_t* prefix_lens, const int32_t* page_table, int max_pages,
+                              int batch, void* cache, int page_size, const RopeFreq& freq,
+                              hipStream_t st);
+
 // ---- per-head GEMMs --------------------------------------------------------
 // abuf[t][h][0:dc] = W_uk_h q_nope[t][h]; abuf[t][h][dc:] = rot(q_rope, pos_t);
 // bf16 layers store both parts multiplied by qscale (softmax scale * log2 e).
@@ -47,10 +59,11 @@ struct SplitPlan {
   int RQ;       // row groups per sequence (bf16 path)
   int NB;       // bf16 path: 1 = one 32-row block per workgroup, 8 = 64-row eight-wave kernel
 };
+// fp8: the cache holds MLA_CACHE_FP8 pages (bf16 layers).
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
-                    float scale, float* opart, float* lse, hipStream_t st);
+                    float scale, float* opart, float* lse, bool fp8, hipStream_t st);
 // out[t][h][:] = (LSE-weighted merge of the split partials) . W_uv_h, one
 // workgroup per (32 query tokens, head); bf16 layers, at most kCombineMaxSplits.
 constexpr int kCombineMaxSplits = 64;
@@ -61,7 +74,7 @@ void launch_combine_out(const SplitPlan& plan, const float* opart, const float* 
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, float* opart,
-                       float* lse, hipStream_t st);
+                       float* lse, bool fp8, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

@@ -40,15 +40,22 @@ constexpr int kNBuf = 4;                      // tiles resident in LDS (3 in fli
 constexpr int kQkRing = 3;                    // score-operand read groups in flight
 constexpr int kPvRing = 6;                    // value-operand reads in flight
 
-template <int NB>
+// F8: MLA_CACHE_FP8 pages.  Waves 1-3 copy each FP8 tile to one of two
+// staging buffers (seven 1 KB copies each) and convert it into the bf16 tile
+// ring (three tiles), a third each, while the score wave scores the tile
+// before it and the value waves use the one before that.
+template <int NB, bool F8>
 __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
-    const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
+    const bf16* __restrict__ abuf, const void* __restrict__ cache_v, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
     float* __restrict__ opart, float* __restrict__ lse) {
   static_assert(NB == 1, "one 32-row block per workgroup");
   constexpr int kDbPerPv = kDC / 32 / 2;       // 32-wide value blocks per value wave (8)
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[kNBuf][kTileTok * kD];
+  constexpr int kBuf = F8 ? 3 : kNBuf;
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[kBuf][kTileTok * kD];
+  __shared__ __attribute__((aligned(1024))) char stage[F8 ? 2 : 1][F8 ? kF8StageBytes : 16];
+  const bf16* __restrict__ cache = reinterpret_cast<const bf16*>(cache_v);
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NB][2][64];
   __shared__ float alpha_s[2][NB][32];
   __shared__ float lrow_s[NB][32];
@@ -100,9 +107,37 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
     const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
     const uint32_t lds0 =
-        lds_tiles + (uint32_t)((it % kNBuf) * kTileBytes + wave * kDmaPerWave * 1024);
+        lds_tiles + (uint32_t)((it % kBuf) * kTileBytes + wave * kDmaPerWave * 1024);
 #pragma unroll
     for (int u = 0; u < kDmaPerWave; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
+  };
+  // FP8 (waves 1-3): this wave's seven of tile `it`'s 21 copies into staging
+  // buffer it & 1 (wave 1 also the scales), and its third of the conversion
+  // of a staged tile into tiles[it % 3]
+  const int cw = wave - 1;
+  auto f8_issue_part = [&](int it) {
+    const int tok0 = tok_begin + it * kTileTok;
+    const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(cache_v) + (int64_t)page * page_size * (kF8Row + 4);
+    const uint8_t* rows = pg + (int64_t)(tok0 % page_size) * kF8Row;
+    const uint32_t dst = lds_address(&stage[it & 1][0]);
+    const int n = cw == 0 ? 6 : 7;            // 6 + 7 + 7 row blocks, and the scales
+    const int blk0 = cw == 0 ? 0 : 6 + 7 * (cw - 1);
+#pragma unroll
+    for (int u = 0; u < 7; ++u) {
+      if (u < n) {
+        const int blk = blk0 + u;
+        dma16(rows, (uint32_t)((blk * 64 + lane) * 16),
+              __builtin_amdgcn_readfirstlane(dst + (uint32_t)blk * 1024u));
+      }
+    }
+    if (cw == 0)
+      dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
+            dst + kF8RowsBytes);
+  };
+  auto f8_convert_part = [&](int it) {
+    f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
+                  tok_end - (tok_begin + it * kTileTok), 64 * cw + lane, 192);
   };
 
   // ---- score waves: their 32 rows of the score operand, in registers
@@ -158,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   // several MFMA groups long under load), so the matrix core never waits on a
   // read issued just before it.
   auto score_tile = [&](int it) {
-    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf][0]);
+    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kBuf][0]);
     const int tok0 = tok_begin + it * kTileTok;
     constexpr int kGroups = kD / 64;          // 9 groups of 4 k-steps
     bf16x8 ring[kQkRing][4];
@@ -198,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   // O^T[dim][row] += sum_tok tile[tok][dim] P[row][tok] over this value wave's
   // 256 dims: 16 (k-step, dim block) steps, transposed reads kPvRing steps ahead.
   auto value_tile = [&](int it) {
-    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kNBuf][0]);
+    const char* tileb = reinterpret_cast<const char*>(&tiles[it % kBuf][0]);
     constexpr int kSteps = 2 * kDbPerPv;
     auto frag_addr = [&](int step, int hl) {
       const int ks = step / kDbPerPv, db = step % kDbPerPv;
@@ -255,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   auto zero_tail = [&](int it) {
     const int nvalid = tok_end - (tok_begin + it * kTileTok);
     if (nvalid < kTileTok) {
-      u32x4* rows = reinterpret_cast<u32x4*>(&tiles[it % kNBuf][0]) + nvalid * kChunks;
+      u32x4* rows = reinterpret_cast<u32x4*>(&tiles[it % kBuf][0]) + nvalid * kChunks;
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int i = threadIdx.x; i < (kTileTok - nvalid) * kChunks; i += blockDim.x) rows[i] = z;
       __syncthreads();
@@ -263,20 +298,60 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
   };
 
   // ---- pipeline: score waves run one tile ahead of value waves
-  for (int p = 0; p < kNBuf - 1; ++p)
-    if (p < ntiles) issue_tile(p);
-  wait_tiles_ahead(min(kNBuf - 2, ntiles - 1));
-  __syncthreads();
-  zero_tail(0);
-  if (score_wave) score_tile(0);
-  for (int it = 0; it < ntiles; ++it) {
-    // tile it+1 must have landed: tiles issued after it are min(ntiles-1, it+2) - (it+1)
-    wait_tiles_ahead(min(ntiles - 1, it + kNBuf - 2) - (it + 1));
-    __syncthreads();   // P(it) and tile it+1 visible; tile it-1 fully consumed
-    if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
-    if (it + 1 < ntiles) zero_tail(it + 1);
-    if (score_wave && it + 1 < ntiles) score_tile(it + 1);
-    if (value_wave) value_tile(it);
+  if constexpr (F8) {
+    // every copy is issued by waves 1-3; before each barrier a wave waits for
+    // its own copies (all seven per tile land in order) and its own LDS writes
+    const bool copier = wave >= 1;
+    if (copier) {
+      f8_issue_part(0);
+      if (ntiles > 1) {
+        f8_issue_part(1);
+        wait_vmcnt<7>();                        // tile 0's copies (tile 1's may fly)
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    __syncthreads();                            // staged tile 0 complete
+    if (copier) {
+      f8_convert_part(0);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+    }
+    __syncthreads();                            // tile 0 converted, staged tile 1 complete
+    if (copier) {
+      if (ntiles > 2) f8_issue_part(2);         // into staging 0 (tile 0 is converted)
+      if (ntiles > 1) f8_convert_part(1);
+    }
+    if (score_wave) score_tile(0);
+    for (int it = 0; it < ntiles; ++it) {
+      if (copier) {
+        wait_vmcnt<0>();                        // staged tile it+2 landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);     // own conversion of tile it+1 written
+      }
+      __syncthreads();   // P(it) and tile it+1 visible; tile it-1 fully consumed
+      if (copier) {
+        if (it + 3 < ntiles) f8_issue_part(it + 3);   // staging of tile it+1, converted already
+        if (it + 2 < ntiles) f8_convert_part(it + 2);  // into tiles[(it - 1) % 3]
+      }
+      if (score_wave && it + 1 < ntiles) score_tile(it + 1);
+      if (value_wave) value_tile(it);
+    }
+  } else {
+    for (int p = 0; p < kNBuf - 1; ++p)
+      if (p < ntiles) issue_tile(p);
+    wait_tiles_ahead(min(kNBuf - 2, ntiles - 1));
+    __syncthreads();
+    zero_tail(0);
+    if (score_wave) score_tile(0);
+    for (int it = 0; it < ntiles; ++it) {
+      // tile it+1 must have landed: tiles issued after it are min(ntiles-1, it+2) - (it+1)
+      wait_tiles_ahead(min(ntiles - 1, it + kNBuf - 2) - (it + 1));
+      __syncthreads();   // P(it) and tile it+1 visible; tile it-1 fully consumed
+      if (it + kNBuf - 1 < ntiles) issue_tile(it + kNBuf - 1);
+      if (it + 1 < ntiles) zero_tail(it + 1);
+      if (score_wave && it + 1 < ntiles) score_tile(it + 1);
+      if (value_wave) value_tile(it);
+    }
   }
   if (value_wave) pv_drain<NB, kDbPerPv>(O);
 
@@ -443,7 +518,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
-                    float scale, float* opart, float* lse, hipStream_t st) {
+                    float scale, float* opart, float* lse, bool fp8, hipStream_t st) {
   // bf16 layers: the absorbed queries already carry scale * log2(e)
   const float scale_log2e = elem == 2 ? 1.f : scale * 1.4426950408889634f;
   if (elem == 2) {
@@ -451,12 +526,17 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
     switch (plan.NB) {
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                          page_size, opart, lse, st);
+                          page_size, opart, lse, fp8, st);
         break;
       default:
-        splitkv_bf16_kernel<1><<<nblocks, 256, 0, st>>>(
-            (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-            page_size, plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
+        if (fp8)
+          splitkv_bf16_kernel<1, true><<<nblocks, 256, 0, st>>>(
+              (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
+              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
+        else
+          splitkv_bf16_kernel<1, false><<<nblocks, 256, 0, st>>>(
+              (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
+              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
         break;
     }
   } else {

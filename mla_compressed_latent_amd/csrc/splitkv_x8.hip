@@ -24,7 +24,12 @@
 //     issue the tile copies (global_load_lds, 9 per wave per tile) and work
 //     one tile behind the score waves.
 // One barrier per tile publishes the tile that landed and the probabilities
-// of the previous one.  Score and value waves run separate loops with the same
+// of the previous one.
+//
+// F8 (MLA_CACHE_FP8 pages): three bf16 tiles and two FP8 staging buffers; the
+// value waves copy each FP8 tile to staging one tile ahead and, besides their
+// value product for tile it-1, convert tile it+1 (a quarter each) while the
+// score waves use tile it.  Score and value waves run separate loops with the same
 // barrier sequence, so their operands (query, O) can share the AGPR file.
 #include "attn_tile.hpp"
 #include "common.hpp"
@@ -39,12 +44,16 @@ constexpr int kX8Dma = kTileBytes / 16 / 64 / 4;        // 9 copies per value wa
 constexpr int kQSteps = kD / 32;                        // 18 k-steps of the 16x16x32 score product
 constexpr int kX8Ring = 6;                              // k-steps of tile reads in flight (2 reads each)
 
+template <bool F8>
 __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
-    const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
+    const bf16* __restrict__ abuf, const void* __restrict__ cache_v, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
     float* __restrict__ opart, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[kX8Buf][kTileTok * kD];
+  constexpr int kBuf = F8 ? 3 : kX8Buf;
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[kBuf][kTileTok * kD];
+  __shared__ __attribute__((aligned(1024))) char stage[F8 ? 2 : 1][F8 ? kF8StageBytes : 16];
+  const bf16* __restrict__ cache = reinterpret_cast<const bf16*>(cache_v);
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][4][64];   // [tile parity][2 rb + ks][lane]
   __shared__ float alpha_s[2][kX8Rows];   // rescale factor of O per row, per tile parity
   __shared__ float lrow_s[kX8Rows];       // row sums at the end
@@ -117,10 +126,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
     const int fb = 2 * (wave >> 1);
     float m_run = -INFINITY, l_run = 0.f;
 
+    if constexpr (F8) __syncthreads();   // the value waves' staging prologue
     for (int it = 0; it <= ntiles; ++it) {
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
       if (it == ntiles) break;
-      const char* tileb = reinterpret_cast<const char*>(&tiles[it % kX8Buf][0]);
+      const char* tileb = reinterpret_cast<const char*>(&tiles[it % kBuf][0]);
       f32x4 acc[2];
       {
         bf16x8 ring[kX8Ring][2];
@@ -201,9 +211,30 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
       const bf16* base = cache + ((int64_t)page * page_size + (tok0 % page_size)) * kD;
       const uint32_t lds0 =
-          lds_tiles + (uint32_t)((it % kX8Buf) * kTileBytes + v * kX8Dma * 1024);
+          lds_tiles + (uint32_t)((it % kBuf) * kTileBytes + v * kX8Dma * 1024);
 #pragma unroll
       for (int u = 0; u < kX8Dma; ++u) dma16(base, dma_off[u], lds0 + u * 1024);
+    };
+    // FP8: this wave's share of tile it's copies into staging buffer it & 1
+    // (five of the twenty 1 KB row blocks; wave 0 also the scales)
+    auto f8_issue_part = [&](int it) {
+      const int tok0 = tok_begin + it * kTileTok;
+      const int page = __builtin_amdgcn_readfirstlane(pages_s[tok0 / page_size - page0]);
+      const uint8_t* pg = reinterpret_cast<const uint8_t*>(cache_v) + (int64_t)page * page_size * (kF8Row + 4);
+      const uint8_t* rows = pg + (int64_t)(tok0 % page_size) * kF8Row;
+      const uint32_t dst = lds_address(&stage[it & 1][0]);
+#pragma unroll
+      for (int u = 0; u < 5; ++u) {
+        const int blk = 5 * v + u;
+        dma16(rows, (uint32_t)((blk * 64 + lane) * 16), dst + blk * 1024);
+      }
+      if (v == 0)
+        dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
+              dst + kF8RowsBytes);
+    };
+    auto f8_convert_tile = [&](int it) {
+      f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
+                 tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256);
     };
     // value operand (transposing read, natural token order): in 16-lane group
     // G, source lane 4 j + q points at dims 4q..4q+3 of the group's 16 dims,
@@ -255,19 +286,41 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         }
     };
 
-    issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    if constexpr (F8) {
+      f8_issue_part(0);
+      if (ntiles > 1) f8_issue_part(1);
+      if (ntiles > 1) {
+        if (v == 0) wait_vmcnt<6>();
+        else wait_vmcnt<5>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();   // staged tile 0 complete
+      f8_convert_tile(0);
+    } else {
+      issue_tile(0);
+      if (ntiles > 1) issue_tile(1);
+    }
     for (int it = 0; it <= ntiles; ++it) {
-      if (it < ntiles) {
+      if constexpr (F8) {
+        // own copies of tile it+1 landed; own conversion writes of tile it done
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+      } else if (it < ntiles) {
         if (it + 1 < ntiles) wait_vmcnt<kX8Dma>();
         else wait_vmcnt<0>();
       }
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
-      if (it + 2 < ntiles) issue_tile(it + 2);
+      if constexpr (F8) {
+        if (it + 2 < ntiles) f8_issue_part(it + 2);   // staging of tile it, converted already
+        if (it + 1 < ntiles) f8_convert_tile(it + 1);   // into tiles[(it - 2) % 3]
+      } else {
+        if (it + 2 < ntiles) issue_tile(it + 2);
+      }
       // then the LDS reads (probabilities, rescale factors, value operands of
       // the first half), whose latency runs under the tail-zeroing below
       const int pt = (it - 1) & 1;
-      const char* tb = reinterpret_cast<const char*>(&tiles[(it + kX8Buf - 1) % kX8Buf][0]);
+      const char* tb = reinterpret_cast<const char*>(&tiles[(it + kBuf - 1) % kBuf][0]);
       bf16x8 pb[2][2];
       float al[2];
       v4bf16 f0[2][2][2];
@@ -280,12 +333,13 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         for (int rb = 0; rb < 2; ++rb) al[rb] = alpha_s[pt][32 * rb + l32];
         load_pv_operands(tb, 0, f0);
       }
-      if (it < ntiles) {
+      if (!F8 && it < ntiles) {
         // rows past the sequence's end hold whatever the page held; zero their
-        // value columns so that zero probabilities never meet a NaN
+        // value columns so that zero probabilities never meet a NaN (the FP8
+        // conversion writes those rows as zeros itself)
         const int nvalid = tok_end - (tok_begin + it * kTileTok);
         if (nvalid < kTileTok) {
-          char* tz = reinterpret_cast<char*>(&tiles[it % kX8Buf][0]);
+          char* tz = reinterpret_cast<char*>(&tiles[it % kBuf][0]);
           const u32x4 z = {0u, 0u, 0u, 0u};
           for (int i = threadIdx.x - 256; i < (kTileTok - nvalid) * (kDC / 8); i += 256)
             *reinterpret_cast<u32x4*>(tz + (nvalid + i / (kDC / 8)) * kD * 2 + (i % (kDC / 8)) * 16) = z;
@@ -338,11 +392,16 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, float* opart,
-                       float* lse, hipStream_t st) {
+                       float* lse, bool fp8, hipStream_t st) {
   const int nblocks = batch * plan.S_max * plan.RQ;
-  splitkv_bf16_x8_kernel<<<nblocks, 512, 0, st>>>(
-      (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
+  if (fp8)
+    splitkv_bf16_x8_kernel<true><<<nblocks, 512, 0, st>>>(
+        (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
+        plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
+  else
+    splitkv_bf16_x8_kernel<false><<<nblocks, 512, 0, st>>>(
+        (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
+        plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
 }
 
 }  // namespace mla

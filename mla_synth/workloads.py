@@ -69,6 +69,7 @@ class Shape:
     dtype: str = "bf16"          # "bf16" or "f32": storage dtype of every tensor
     rope_base: float = 10000.0
     page_size: int = 64
+    cache_format: str = "dtype"  # "dtype": rows in dtype; "fp8": 8-bit float latent pages
 
     # short aliases
     @property
@@ -95,6 +96,13 @@ class Shape:
     def row_width(self) -> int:
         """Elements in one cached row: the latent followed by the rope key."""
         return self.kv_lora_rank + self.qk_rope_head_dim
+
+    @property
+    def cache_token_bytes(self) -> int:
+        """Bytes one cached token takes in a page (row, plus its scale for fp8)."""
+        if self.cache_format == "fp8":
+            return 512 + 2 * self.qk_rope_head_dim + 4
+        return self.row_width * self.elem_bytes
 
     @property
     def elem_bytes(self) -> int:
@@ -259,6 +267,16 @@ WORKLOADS = {
         fixed_prefix=None, max_prefix=32768, fixed_q_len=None, max_q_len=2, spare_page_frac=0.05,
         description="bf16; DeepSeek-V2 shape, 256 sequences, prefix ~ U[1, 32768], q_len ~ U{1,2}, "
                     "64-token pages under a random page table, new tokens appended first"),
+    "dsv2_b32_ctx4096_fp8": Workload(
+        "dsv2_b32_ctx4096_fp8", replace(DSV2, cache_format="fp8"), batch=32, seed=2, prefix_source="hidden",
+        fixed_prefix=4095,
+        description="bf16 layer over an FP8 latent cache (E4M3 codes, per-row power-of-two scale); "
+                    "DeepSeek-V2 shape, batch 32, every context 4096, q_len 1"),
+    "llama2_7b_mla_b64_ctx8192_fp8": Workload(
+        "llama2_7b_mla_b64_ctx8192_fp8", replace(LLAMA2_7B_MLA, cache_format="fp8"), batch=64, seed=3,
+        prefix_source="hidden", fixed_prefix=8191,
+        description="bf16 layer over an FP8 latent cache; Llama-2-7B shape with a 512-wide latent, "
+                    "batch 64, every context 8192"),
     "dsv2_60layers_b32_ctx4096": Workload(
         "dsv2_60layers_b32_ctx4096", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
         layers=60,

@@ -59,6 +59,28 @@ def e4m3_encode(x: float) -> int:
     return sign | best_code
 
 
+_MAG_VALUES = np.array([v for v, _ in _MAGS])   # ascending; index = code
+
+
+def e4m3_encode_array(x) -> np.ndarray:
+    """e4m3_encode over an array: the two codes around |x| by a sorted
+    search, the nearer one, ties to the even code, sign bit from x."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.size and (not np.all(np.isfinite(x)) or np.abs(x).max() > E4M3_MAX):
+        raise ValueError("outside the E4M3 range")
+    a = np.abs(x)
+    hi = np.minimum(np.searchsorted(_MAG_VALUES, a, side="left"), len(_MAG_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _MAG_VALUES[lo]
+    dhi = _MAG_VALUES[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 7)
+
+
+DECODE_TABLE = np.array([e4m3_decode(c) for c in range(256)])
+
+
 def row_scale_exponent(amax: float) -> int:
     """Smallest integer e with amax <= 448 * 2^e (0 when amax is 0)."""
     if amax == 0.0:
@@ -76,12 +98,11 @@ def quantize_row(c) -> tuple[np.ndarray, int]:
     """Codes (uint8) and scale exponent of one latent row."""
     c = np.asarray(c, dtype=np.float64)
     e = row_scale_exponent(float(np.abs(c).max()) if c.size else 0.0)
-    codes = np.array([e4m3_encode(v * 2.0 ** -e) for v in c], dtype=np.uint8)
-    return codes, e
+    return e4m3_encode_array(c * 2.0 ** -e), e
 
 
 def dequantize_row(codes, e: int) -> np.ndarray:
-    return np.array([e4m3_decode(int(k)) for k in codes], dtype=np.float64) * 2.0 ** e
+    return DECODE_TABLE[np.asarray(codes, dtype=np.uint8)] * 2.0 ** e
 
 
 def fp8_rows(rows: np.ndarray, d_c: int) -> np.ndarray:

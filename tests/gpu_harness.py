@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from mla_synth import Workload
-from oracle import mla_oracle
+from oracle import fp8, mla_oracle
 
 SENTINEL_BYTE = 0xA5
 
@@ -45,7 +45,11 @@ class GpuCase:
         self.table_np = table
         self.page_table = i32(table)
         self.num_pages = num_pages
-        self.cache = torch.empty((num_pages, s.page_size, s.row_width), dtype=dt, device=dev)
+        if s.cache_format == "fp8":   # pages of 640-byte rows, then the rows' fp32 scales
+            self.cache = torch.empty((num_pages, s.page_size * s.cache_token_bytes), dtype=torch.uint8,
+                                     device=dev)
+        else:
+            self.cache = torch.empty((num_pages, s.page_size, s.row_width), dtype=dt, device=dev)
         if fill_sentinel:
             self.cache.view(torch.uint8).fill_(SENTINEL_BYTE)
         self.prefix = wl.prefix_lens()
@@ -81,6 +85,8 @@ class GpuCase:
                 mla.mla_append_latent(self.layer, x, i32(cu), i32(np.zeros(B)), self.page_table, self.cache)
                 del x
         else:
+            if wl.shape.cache_format == "fp8":
+                raise ValueError("fp8 caches are filled through the append path (hidden prefixes)")
             ps = wl.shape.page_size
             futs = {b: pool.submit(wl.prefix_latent, b) for b in range(min(B, 16))}
             for b in range(B):
@@ -125,8 +131,10 @@ class GpuCase:
         return rows[:L]
 
 
-def oracle_cache(wl: Workload, b: int, w_dkv=None) -> np.ndarray:
-    """The oracle's float64 rows of sequence b after the new tokens are appended."""
+def oracle_cache(wl: Workload, b: int, w_dkv=None, quantize=True) -> np.ndarray:
+    """The oracle's float64 rows of sequence b after the new tokens are
+    appended (for an fp8 cache: with the latent quantized and dequantized by
+    the oracle's own row quantizer, unless quantize is False)."""
     s = wl.shape
     w_dkv = wl.w_dkv() if w_dkv is None else w_dkv
     P = int(wl.prefix_lens()[b])
@@ -135,7 +143,10 @@ def oracle_cache(wl: Workload, b: int, w_dkv=None) -> np.ndarray:
     else:
         pre = wl.prefix_latent(b).astype(np.float64)
     new = mla_oracle.latent_rows(wl.new_hidden(b), w_dkv, P + np.arange(int(wl.q_lens()[b])), s.d_c, s.rope_base)
-    return np.concatenate([pre, new], axis=0)
+    rows = np.concatenate([pre, new], axis=0)
+    if s.cache_format == "fp8" and quantize:
+        rows = fp8.fp8_rows(rows, s.d_c)
+    return rows
 
 
 def oracle_outputs(wl: Workload, b: int, heads=None, w_dkv=None, w_uk=None, w_uv=None) -> np.ndarray:

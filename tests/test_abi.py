@@ -136,3 +136,25 @@ def test_extend_rejects_null_layer(mla):
     assert mla.lib.mla_extend_workspace_bytes(None, 1, 1, 1, 1, 0) == 0
     st = mla.lib.mla_extend(None, None, None, None, None, 1, 1, 1, 1, 1, 0, None, 1, None, None, 0, None)
     assert st == 1 and "null" in mla.mla_last_error()
+
+
+def test_fp8_cache_format(mla):
+    """MLA_CACHE_FP8: 512 code bytes + 64 bf16 rope + a 4-byte scale per token;
+    bf16 layers only; unknown formats rejected."""
+    assert mla.mla_cache_bytes_per_token(_cfg(mla, cache_format=1)) == 512 + 128 + 4
+    assert mla.mla_cache_bytes_per_token(_cfg(mla, cache_format=0)) == 1152
+    tiny = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                v_head_dim=16, kv_lora_rank=32, dtype=0, cache_format=1)
+    assert mla.mla_cache_bytes_per_token(tiny) == 0
+    assert mla.mla_folded_bytes(_cfg(mla, cache_format=2)) == 0
+    h = ctypes.c_void_p()
+    st = mla.lib.mla_fold_weights(ctypes.byref(tiny), ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                  ctypes.c_void_p(256), 1 << 40, None, ctypes.byref(h))
+    assert st == 2 and "bf16" in mla.mla_last_error()
+    # the expanded extend form reads bf16 rows: AUTO keeps FP8 layers absorbed
+    assert mla.mla_extend_choose_path(_cfg(mla, cache_format=1), 2, 8192, 4096, 4096) == mla.MLA_EXTEND_ABSORBED
+    # capacity: the same budget holds 1152 / 644 times more tokens
+    GIB = 1 << 30
+    n8 = mla.mla_plan_max_sequences(_cfg(mla, cache_format=1), 60, 80 * GIB, 32768)
+    assert n8 == (80 * GIB) // (60 * 32768 * 644)
+    assert mla.mla_plan_max_sequences(_cfg(mla), 60, 80 * GIB, 32768) == 37

@@ -71,3 +71,15 @@ def test_quantize_row_error_bound():
         assert np.abs(d).max() > 224.0 * 2.0 ** e * 0.99 or np.abs(c).max() <= 224.0 * 2.0 ** e
     codes, e = fp8.quantize_row(np.zeros(8))
     assert e == 0 and not codes.any()
+
+
+def test_array_encoder_is_the_scalar_definition():
+    rng = np.random.default_rng(1)
+    mids = [(fp8.e4m3_decode(c) + fp8.e4m3_decode(c + 1)) / 2 for c in range(0x7E)]
+    x = np.concatenate([rng.uniform(-448, 448, 2000), rng.standard_normal(2000) * 0.01,
+                        np.array(mids), -np.array(mids), [0.0, -0.0, 448.0, -448.0, 2.0 ** -10]])
+    got = fp8.e4m3_encode_array(x)
+    want = np.array([fp8.e4m3_encode(v) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, want)
+    assert np.array_equal(fp8.dequantize_row(np.arange(256, dtype=np.uint8), 3)[:0x7F],
+                          np.array([fp8.e4m3_decode(c) * 8.0 for c in range(0x7F)]))
