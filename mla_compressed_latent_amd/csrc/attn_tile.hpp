@@ -95,19 +95,21 @@ __device__ __forceinline__ void f8_issue(const uint8_t* page, int page_size, int
 }
 
 // Items item0, item0 + istep, ... of one staged tile into the bf16 tile:
-// latent items 0..1023 (row i / 32, codes 16 (i % 32) .. + 15 -> bf16 chunks
-// 2 (i % 32) and + 1) and rope items 0..255 (row i / 8, chunk 64 + i % 8).
+// latent items below latent_end of 0..1023 (row i / 32, codes 16 (i % 32) ..
+// + 15 -> bf16 chunks 2 (i % 32) and + 1) and rope items from rope_begin of
+// 0..255 (row i / 8, chunk 64 + i % 8).
 // Rows at or past nvalid are written as zeros, so that zero probabilities
 // never meet whatever the page held there.  U items per lane go at a time:
 // all their staging reads first, so that the LDS latency is paid once per
 // batch rather than once per item.
 template <int U>
 __device__ __forceinline__ void f8_convert(const char* stage, char* tile, int nvalid, int item0,
-                                           int istep) {
+                                           int istep, int latent_end = kTileTok * 32,
+                                           int rope_begin = 0) {
   const float* scales = reinterpret_cast<const float*>(stage + kF8RowsBytes);
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll 1
-  for (int base = item0; base < kTileTok * 32; base += U * istep) {
+  for (int base = item0; base < latent_end; base += U * istep) {
     u32x4 w[U];
     float sc[U];
 #pragma unroll
@@ -115,7 +117,7 @@ __device__ __forceinline__ void f8_convert(const char* stage, char* tile, int nv
       const int i = base + u * istep, t = i >> 5;
       w[u] = zero;
       sc[u] = 0.f;
-      if (i < kTileTok * 32 && t < nvalid) {
+      if (i < latent_end && t < nvalid) {
         w[u] = *reinterpret_cast<const u32x4*>(stage + t * kF8Row + (i & 31) * 16);
         sc[u] = scales[t];
       }
@@ -123,7 +125,7 @@ __device__ __forceinline__ void f8_convert(const char* stage, char* tile, int nv
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = base + u * istep, t = i >> 5, k = i & 31;
-      if (i >= kTileTok * 32) break;
+      if (i >= latent_end) break;
       u32x4 lo = zero, hi = zero;
       if (t < nvalid) {
 #pragma unroll
@@ -146,7 +148,7 @@ __device__ __forceinline__ void f8_convert(const char* stage, char* tile, int nv
     }
   }
 #pragma unroll 1
-  for (int base = item0; base < kTileTok * 8; base += U * istep) {
+  for (int base = rope_begin + item0; base < kTileTok * 8; base += U * istep) {
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {

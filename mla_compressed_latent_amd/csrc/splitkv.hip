@@ -135,9 +135,15 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
       dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
             dst + kF8RowsBytes);
   };
+  // wave 1 has no other work: it converts latent items 0..511 and every rope
+  // item; the value waves 512..767 and 768..1023
   auto f8_convert_part = [&](int it) {
-    f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
-                  tok_end - (tok_begin + it * kTileTok), 64 * cw + lane, 192);
+    char* dst = reinterpret_cast<char*>(&tiles[it % kBuf][0]);
+    const int nvalid = tok_end - (tok_begin + it * kTileTok);
+    if (cw == 0)
+      f8_convert<8>(&stage[it & 1][0], dst, nvalid, lane, 64, 512, 0);
+    else
+      f8_convert<4>(&stage[it & 1][0], dst, nvalid, 256 + 256 * cw + lane, 64, 512 + 256 * cw, 256);
   };
 
   // ---- score waves: their 32 rows of the score operand, in registers

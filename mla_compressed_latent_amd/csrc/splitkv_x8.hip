@@ -128,6 +128,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
 
     if constexpr (F8) __syncthreads();   // the value waves' staging prologue
     for (int it = 0; it <= ntiles; ++it) {
+      if constexpr (F8) __builtin_amdgcn_s_waitcnt(0xc07f);   // own conversion writes done
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
       if (it == ntiles) break;
       const char* tileb = reinterpret_cast<const char*>(&tiles[it % kBuf][0]);
@@ -188,6 +189,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       l_run = l_run * alpha + rs;
       m_run = m_new;
       if (G == 0) alpha_s[it & 1][16 * wave + c16] = alpha;
+      if constexpr (F8)
+        if (it + 1 < ntiles)   // latent items 512..1023 of the next tile (value waves: the rest)
+          f8_convert<2>(&stage[(it + 1) & 1][0], reinterpret_cast<char*>(&tiles[(it + 1) % kBuf][0]),
+                        tok_end - (tok_begin + (it + 1) * kTileTok), 512 + 64 * wave + lane, 256,
+                        kTileTok * 32, 256);
     }
     if (G == 0) lrow_s[16 * wave + c16] = l_run;
     __syncthreads();   // row sums published
@@ -232,9 +238,12 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
               dst + kF8RowsBytes);
     };
+    // tile 0 (prologue): all latent items; later tiles: items 0..511 and the
+    // rope items (the score waves convert 512..1023)
     auto f8_convert_tile = [&](int it) {
       f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
-                 tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256);
+                    tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256,
+                    it == 0 ? kTileTok * 32 : 512, 0);
     };
     // value operand (transposing read, natural token order): in 16-lane group
     // G, source lane 4 j + q points at dims 4q..4q+3 of the group's 16 dims,
