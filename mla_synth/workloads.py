@@ -31,6 +31,7 @@ STREAM_CTX = 5
 STREAM_QLEN = 6
 STREAM_PAGES = 7
 STREAM_Q = 8
+STREAM_W_O = 9
 
 
 # ---------------------------------------------------------------- bf16 I/O --
@@ -189,6 +190,11 @@ class Workload:
     def w_uv(self) -> np.ndarray:
         s = self.shape
         return self._normal(self.rng(STREAM_W_UV), (s.d_c, s.H * s.d_v), 1.0 / np.sqrt(s.d_c))
+
+    def w_o(self) -> np.ndarray:
+        """Output projection [H * d_v][d_model]: concatenated heads -> hidden size."""
+        s = self.shape
+        return self._normal(self.rng(STREAM_W_O), (s.H * s.d_v, s.d_model), 1.0 / np.sqrt(s.H * s.d_v))
 
     # ------------------------------------------------------------ activations
     def prefix_hidden(self, b: int) -> np.ndarray:

@@ -41,7 +41,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * Sequence b holds L_b cached rows after the new tokens are appended; its
   q_len_b queries sit at positions L_b - q_len_b + i and each attends to
   every position not after its own.
-* Output per query and head is ``sum_t w_t V_h[t]`` (no output projection).
+* Output per query and head is ``sum_t w_t V_h[t]`` (no output projection);
+  where a layer output is asked for, it is the concatenated heads times an
+  output projection W_o of shape [H * d_v][d_model] (``project_output``).
 """
 from __future__ import annotations
 
@@ -55,6 +57,7 @@ __all__ = [
     "attend_sequence",
     "decode",
     "default_scale",
+    "project_output",
 ]
 
 
@@ -161,3 +164,13 @@ def decode(q: np.ndarray, caches, w_uk, w_uv, q_lens, n_heads: int, d_nope: int,
                                     base, scale))
         off += lq
     return np.concatenate(outs, axis=0)
+
+
+def project_output(out: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Layer output y[t] = concat_h out[t][h] . W_o for out [Tq][H][d_v] and
+    W_o [H * d_v][d_model] ("Multi-head Latent Attention and KV Cache
+    Compression", section "The absorption trick and decoupled RoPE": the value
+    up-projection can be folded into this output projection)."""
+    out = np.asarray(out, dtype=np.float64)
+    tq, h, dv = out.shape
+    return out.reshape(tq, h * dv) @ np.asarray(w_o, dtype=np.float64)
