@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("auto", "absorbed", "expanded"), default="auto",
                     help="form of mla_extend for extend workloads")
+    ap.add_argument("--form", choices=("auto", "unfolded", "folded"), default="auto",
+                    help="output projection form for project workloads")
     return ap.parse_args()
 
 
@@ -98,7 +100,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_state(wl, kv_chunk, rotate, path="auto"):
+def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
     import numpy as np
     import torch
 
@@ -178,6 +180,14 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
     for _ in range(R - 1):
         layers.append(mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv))
         caches.append(cache0.clone())
+    out_form = None
+    if wl.kind == "project":
+        out_form = {"auto": mla.mla_output_choose_form(cfg, int(wl.q_lens().sum())),
+                    "unfolded": mla.MLA_OUTPUT_UNFOLDED, "folded": mla.MLA_OUTPUT_FOLDED}[form]
+        w_o = up(wl.w_o())
+        for layer in layers:
+            mla.mla_fold_output(layer, w_uv, w_o, out_form)
+        del w_o
     del w_dkv, w_uk, w_uv
     torch.cuda.synchronize()
 
@@ -188,12 +198,17 @@ def build_state(wl, kv_chunk, rotate, path="auto"):
         seq_lens=i32(seq_lens_np), seq_lens_np=seq_lens_np, max_q_len=int(q_lens.max()),
         max_seq_len=int(seq_lens_np.max()), kv_chunk=kv_chunk,
         out=torch.empty((Tq, s.H, s.d_v), dtype=dt, device=dev),
-        cache_bytes=cache_bytes, folded_bytes=folded_bytes, cfg=cfg, pool=pool,
+        cache_bytes=cache_bytes, folded_bytes=folded_bytes, cfg=cfg, pool=pool, out_form=out_form,
     )
     st["chunk"] = mla.mla_decode_kv_chunk(layer0, B, st["max_q_len"], st["max_seq_len"], kv_chunk)
     st["aws"] = torch.empty(max(1, mla.mla_append_workspace_bytes(layer0, Tq)), dtype=torch.uint8, device=dev)
     st["extend"] = wl.kind == "extend"
-    if st["extend"]:
+    st["project"] = wl.kind == "project"
+    if st["project"]:
+        st["y"] = torch.empty((Tq, s.d_model), dtype=dt, device=dev)
+        st["dws"] = torch.empty(max(1, mla.mla_decode_project_workspace_bytes(
+            layer0, B, Tq, st["max_q_len"], st["max_seq_len"])), dtype=torch.uint8, device=dev)
+    elif st["extend"]:
         chosen = mla.mla_extend_choose_path(cfg, B, Tq, st["max_q_len"], st["max_seq_len"])
         st["auto_path"] = chosen
         st["path"] = {"auto": chosen, "absorbed": mla.MLA_EXTEND_ABSORBED,
@@ -212,6 +227,18 @@ def run_step(st, i, ev=None, path=None):
     mla = st["mla"]
     r = i % st["R"]
     layer, cache = st["layers"][r], st["caches"][r]
+    if st["project"]:
+        if ev is not None:
+            ev[0].record()
+        mla.mla_append_latent(layer, st["x_new"], st["cu_q"], st["prefix"], st["table"], cache,
+                              workspace=st["aws"])
+        if ev is not None:
+            ev[1].record()
+        mla.mla_decode_project(layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["y"],
+                               st["max_q_len"], st["max_seq_len"], workspace=st["dws"])
+        if ev is not None:
+            ev[2].record()
+        return
     if st["extend"]:
         if ev is not None:
             ev[0].record()
@@ -335,8 +362,8 @@ def main():
     wl = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     log(f"workload {wl.name}: {wl.description}")
-    st = build_state(wl, args.kv_chunk, args.rotate, args.path)
-    if st["extend"]:
+    st = build_state(wl, args.kv_chunk, args.rotate, args.path, args.form)
+    if st["extend"] or st["project"]:
         return main_extend(args, wl, st)
     log(f"kv_chunk {st['chunk']}, {st['R']} rotated copies of cache ({st['cache_bytes'] / 1e6:.1f} MB) "
         f"+ folded weights ({st['folded_bytes'] / 1e6:.1f} MB)")
@@ -495,6 +522,66 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def main_project(args, wl, st):
+    """Decode + output projection: graph replay of append + mla_decode_project."""
+    import torch
+
+    mla = st["mla"]
+    s = st["s"]
+    K = args.steps
+    n = min(K, 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        run_step(st, i, evs[i])
+    torch.cuda.synchronize()
+    phase = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / n for j in range(2)]
+    R = st["R"]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all, stream=cap):
+            for r in range(R):
+                run_step(st, r)
+    torch.cuda.current_stream().wait_stream(cap)
+    g_all.replay()
+    torch.cuda.synchronize()
+    reps = max(1, K // R)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        g_all.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / (reps * R)
+    folded = st["out_form"] == mla.MLA_OUTPUT_FOLDED
+    H, dc, dv, dm = s.H, s.d_c, s.d_v, s.d_model
+    w_bytes = 2 * H * dc * dm if folded else 2 * H * dv * (dc + dm)
+    latent = int(st["seq_lens_np"].astype("int64").sum()) * s.cache_token_bytes
+    call_s = phase[1] * 1e-3
+    achieved = (latent + w_bytes + 2 * H * dc * s.d_nope) / call_s / 1e9
+    res = {
+        "metric": "MLA decode + output projection tokens/s, 1 GPU", "value": st["Tq"] / (ms_step * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": reps * R, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic (seeded Gaussian hidden states and weights)",
+        "config": {"workload": wl.name, "batch": wl.batch, "query_tokens": st["Tq"],
+                   "max_context": st["max_seq_len"], "heads": H, "d_model": dm,
+                   "output_form": "folded" if folded else "unfolded", "rotated_copies": R},
+        "timing": "HIP graph replay of whole steps (append + mla_decode_project)",
+        "phase_ms": {"append": phase[0], "decode_project": phase[1]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "mla_decode_project (all its kernels, HIP events around the call)",
+                     "algorithmic_bytes_per_launch": latent + w_bytes + 2 * H * dc * s.d_nope,
+                     "weights_streamed_bytes": w_bytes},
+    }
+    log(f"{ms_step * 1e3:.1f} us/step (graph); decode+project {phase[1] * 1e3:.1f} us "
+        f"({'folded' if folded else 'unfolded'}, weights {w_bytes / 1e6:.0f} MB)")
+    print(json.dumps(res), flush=True)
+
+
 def main_extend(args, wl, st):
     """Chunked extend / prefill: HIP-graph replay of append + mla_extend."""
     import torch
@@ -506,6 +593,8 @@ def main_extend(args, wl, st):
         run_step(st, i)
     torch.cuda.synchronize()
     K = args.steps
+    if st["project"]:
+        return main_project(args, wl, st)
     # eager per-phase times of both forms (the choice's evidence)
     path_ms = {}
     phase = None

@@ -344,6 +344,61 @@ int64_t mla_pool_length(const mla_page_pool* pool, int32_t seq);
 mla_status mla_pool_page_table(const mla_page_pool* pool, const int32_t* seqs, int32_t n,
                                int32_t* table);
 
+/* ---------------------------------------------------------------------------
+ * Layer output with the output projection W_o, the value up-projection kept
+ * apart or folded into it ("Multi-head Latent Attention and KV Cache
+ * Compression", section "The absorption trick and decoupled RoPE": the
+ * value-side up-projection is absorbed into the output projection the same
+ * way the key side is absorbed into the query).
+ *   MLA_OUTPUT_UNFOLDED  y = concat_h(o_lat_h W_uv_h) . W_o
+ *                        (weights H*d_v*(d_c + d_model) elements)
+ *   MLA_OUTPUT_FOLDED    y = concat_h(o_lat_h) . W_uvo, W_uvo_h = W_uv_h W_o_h
+ *                        folded once at load (H*d_c*d_model elements)
+ *   MLA_OUTPUT_AUTO      mla_output_choose_form(cfg, 1)
+ * bf16 layers with num_attention_heads * v_head_dim a multiple of 256.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  MLA_OUTPUT_AUTO = 0,
+  MLA_OUTPUT_UNFOLDED = 1,
+  MLA_OUTPUT_FOLDED = 2
+} mla_output_form;
+
+/* The form with the smaller estimated time for total_q query tokens, each
+ * form's time the larger of its weight bytes / 8 TB/s and its matrix-core
+ * flops / 2.5 PFLOP/s.  Folding wins only when d_model < d_c d_v / (d_c - d_v)
+ * (for d_c > d_v): never for the shapes the kernels take.  Host only; -1 on
+ * an invalid config or total_q < 1. */
+int32_t mla_output_choose_form(const mla_config* cfg, int32_t total_q);
+
+/* Bytes of the buffer mla_fold_output fills for a form (0 if unsupported). */
+size_t mla_output_folded_bytes(const mla_config* cfg, int32_t form);
+
+/* Attach the output projection to a layer.
+ *   w_uv  [d_c][H * d_v]       device, the same W_uv given to mla_fold_weights
+ *                              (read for MLA_OUTPUT_FOLDED only; may be null otherwise)
+ *   w_o   [H * d_v][d_model]   device; head h = rows h*d_v ..
+ *   folded                     device, >= mla_output_folded_bytes(cfg, form),
+ *                              256-byte aligned, kept and read by later calls
+ * The inputs are read by work enqueued on hip_stream.  Errors: INVALID_ARG,
+ * UNSUPPORTED (fp32 layer, H * d_v not a multiple of 256),
+ * INSUFFICIENT_WORKSPACE, HIP. */
+mla_status mla_fold_output(mla_layer* layer, const void* w_uv, const void* w_o, int32_t form,
+                           void* folded, size_t folded_bytes, void* hip_stream);
+
+size_t mla_decode_project_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
+                                          int32_t max_q_len, int32_t max_seq_len);
+
+/* mla_decode (kv_chunk 0) followed by the output projection: y [total_q][d_model]
+ * (layer dtype) = concat_h out[t][h] . W_o, by the form the layer was folded
+ * with.  Same arguments and contract as mla_decode otherwise; the workspace is
+ * scratch for this call only.  Errors as mla_decode, and INVALID_ARG when no
+ * output projection was folded. */
+mla_status mla_decode_project(const mla_layer* layer, const void* q, const int32_t* cu_q,
+                              const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                              int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                              const void* cache, int64_t num_pages, void* y, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 

@@ -23,6 +23,8 @@ __all__ = [
     "MLA_PHASE_ALL", "mla_extend_choose_path", "mla_extend_workspace_bytes", "mla_extend",
     "MLA_EXTEND_AUTO", "MLA_EXTEND_ABSORBED", "MLA_EXTEND_EXPANDED",
     "MlaCachePlan", "mla_plan_cache", "mla_plan_max_sequences", "PagePool", "MLA_CACHE_DTYPE", "MLA_CACHE_FP8",
+    "mla_output_choose_form", "mla_output_folded_bytes", "mla_fold_output", "mla_decode_project_workspace_bytes",
+    "mla_decode_project", "MLA_OUTPUT_AUTO", "MLA_OUTPUT_UNFOLDED", "MLA_OUTPUT_FOLDED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -32,6 +34,7 @@ MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 MLA_PHASE_ABSORB, MLA_PHASE_ATTEND, MLA_PHASE_OUTPUT, MLA_PHASE_ALL = 1, 2, 4, 7
 MLA_EXTEND_AUTO, MLA_EXTEND_ABSORBED, MLA_EXTEND_EXPANDED = 0, 1, 2
 MLA_CACHE_DTYPE, MLA_CACHE_FP8 = 0, 1
+MLA_OUTPUT_AUTO, MLA_OUTPUT_UNFOLDED, MLA_OUTPUT_FOLDED = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
@@ -39,7 +42,9 @@ EXPORTED_SYMBOLS = (
     "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_extend_choose_path",
     "mla_extend_workspace_bytes", "mla_extend", "mla_plan_cache", "mla_plan_max_sequences",
     "mla_pool_create", "mla_pool_destroy", "mla_pool_reserve", "mla_pool_release", "mla_pool_free_pages",
-    "mla_pool_length", "mla_pool_page_table", "mla_status_string", "mla_last_error",
+    "mla_pool_length", "mla_pool_page_table", "mla_output_choose_form", "mla_output_folded_bytes",
+    "mla_fold_output", "mla_decode_project_workspace_bytes", "mla_decode_project", "mla_status_string",
+    "mla_last_error",
 )
 
 
@@ -118,6 +123,11 @@ def _load():
         "mla_pool_free_pages": (I64, [P]),
         "mla_pool_length": (I64, [P, I32]),
         "mla_pool_page_table": (I32, [P, P, I32, P]),
+        "mla_output_choose_form": (I32, [cfgp, I32]),
+        "mla_output_folded_bytes": (S, [cfgp, I32]),
+        "mla_fold_output": (I32, [P, P, P, I32, P, S, P]),
+        "mla_decode_project_workspace_bytes": (S, [P, I32, I32, I32, I32]),
+        "mla_decode_project": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
@@ -366,3 +376,49 @@ class PagePool:
         _check(lib.mla_pool_page_table(self.handle, ids.ctypes.data_as(ctypes.c_void_p), int(ids.shape[0]),
                                        out.ctypes.data_as(ctypes.c_void_p)), "mla_pool_page_table")
         return out
+
+
+def mla_output_choose_form(cfg: MlaConfig, total_q: int) -> int:
+    return int(lib.mla_output_choose_form(ctypes.byref(cfg), int(total_q)))
+
+
+def mla_output_folded_bytes(cfg: MlaConfig, form: int) -> int:
+    return int(lib.mla_output_folded_bytes(ctypes.byref(cfg), int(form)))
+
+
+def mla_fold_output(layer: Layer, w_uv, w_o, form: int = MLA_OUTPUT_AUTO, folded=None, stream=None):
+    """Attach the output projection (W_o, or W_uv W_o folded) to the layer."""
+    dt = layer.cfg.torch_dtype
+    if form == MLA_OUTPUT_AUTO:
+        form = mla_output_choose_form(layer.cfg, 1)
+    n = mla_output_folded_bytes(layer.cfg, form)
+    if folded is None:
+        folded = torch.empty(max(1, n), dtype=torch.uint8, device=w_o.device)
+    _check(lib.mla_fold_output(layer.handle, None if w_uv is None else _dev(w_uv, "w_uv", dt), _dev(w_o, "w_o", dt),
+                               int(form), _dev(folded, "folded"), folded.numel(), _stream(stream)),
+           "mla_fold_output")
+    layer.out_folded = folded     # the layer reads it from now on
+    layer.out_form = form
+    return form
+
+
+def mla_decode_project_workspace_bytes(layer: Layer, batch: int, total_q: int, max_q_len: int,
+                                       max_seq_len: int) -> int:
+    return int(lib.mla_decode_project_workspace_bytes(layer.handle, batch, total_q, max_q_len, max_seq_len))
+
+
+def mla_decode_project(layer: Layer, q, cu_q, seq_lens, page_table, cache, y, max_q_len: int, max_seq_len: int,
+                       workspace=None, stream=None):
+    """Decode plus output projection: y [total_q][d_model]."""
+    dt = layer.cfg.torch_dtype
+    total_q = int(q.shape[0])
+    batch = int(seq_lens.shape[0])
+    if workspace is None:
+        n = mla_decode_project_workspace_bytes(layer, batch, total_q, max_q_len, max_seq_len)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_project(
+        layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
+        int(max_seq_len), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(y, "y", dt),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "mla_decode_project")

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip",
-           "extend.hip", "pool.cpp"]
+           "extend.hip", "project.hip", "pool.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

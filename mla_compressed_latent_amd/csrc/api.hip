@@ -22,6 +22,8 @@ struct mla_layer {
   void* wukt_p;    // bf16: per head, rows i < d_nope, k = j < d_c (expanded path)
   mla::RopeFreq freq;   // rotary frequencies (bf16 layers)
   int num_cus;
+  void* wo_p = nullptr;  // output projection, tiled (mla_fold_output)
+  int out_form = 0;      // MLA_OUTPUT_UNFOLDED or MLA_OUTPUT_FOLDED once folded
 };
 
 namespace {
@@ -475,6 +477,125 @@ mla_status mla_extend(const mla_layer* L, const void* q, const int32_t* cu_q, co
                           max_q_len, H, c.qk_nope_head_dim, c.v_head_dim, c.page_size, e.lmax, L->freq,
                           L->scale, out, st);
   return hip_check("extend launch");
+}
+
+int32_t mla_output_choose_form(const mla_config* cfg, int32_t total_q) {
+  if (check_config(cfg) != MLA_OK || total_q < 1) return -1;
+  // weight bytes streamed and matrix-core flops of the two forms; the time of
+  // each is the larger of bytes / 8 TB/s and flops / 2.5 PFLOP/s
+  const double H = cfg->num_attention_heads, dc = cfg->kv_lora_rank, dv = cfg->v_head_dim;
+  const double dm = cfg->d_model, e = cfg->dtype == MLA_DTYPE_BF16 ? 2.0 : 4.0, T = total_q;
+  const double unf = fmax(e * H * dv * (dc + dm) / 8e12, 2.0 * T * H * dv * (dc + dm) / 2.5e15);
+  const double fol = fmax(e * H * dc * dm / 8e12, 2.0 * T * H * dc * dm / 2.5e15);
+  return fol < unf ? MLA_OUTPUT_FOLDED : MLA_OUTPUT_UNFOLDED;
+}
+
+size_t mla_output_folded_bytes(const mla_config* cfg, int32_t form) {
+  if (check_config(cfg) != MLA_OK || cfg->dtype != MLA_DTYPE_BF16) return 0;
+  const size_t H = cfg->num_attention_heads, dm = cfg->d_model;
+  if (form == MLA_OUTPUT_UNFOLDED) return align256(H * cfg->v_head_dim * dm * 2);
+  if (form == MLA_OUTPUT_FOLDED) return align256(H * cfg->kv_lora_rank * dm * 2);
+  return 0;
+}
+
+mla_status mla_fold_output(mla_layer* L, const void* w_uv, const void* w_o, int32_t form, void* folded,
+                           size_t folded_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  const mla_config& c = L->cfg;
+  if (form == MLA_OUTPUT_AUTO) form = mla_output_choose_form(&c, 1);
+  if (form != MLA_OUTPUT_UNFOLDED && form != MLA_OUTPUT_FOLDED)
+    return fail(MLA_ERR_INVALID_ARG, "mla_fold_output: unknown form %d", form);
+  if (c.dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_output: the projection kernels need a bf16 layer");
+  if ((c.num_attention_heads * c.v_head_dim) % 256)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_output: num_attention_heads * v_head_dim must be a multiple of 256");
+  if (!w_o || !folded || (form == MLA_OUTPUT_FOLDED && !w_uv))
+    return fail(MLA_ERR_INVALID_ARG, "mla_fold_output: null pointer argument");
+  if ((uintptr_t)folded % 256) return fail(MLA_ERR_INVALID_ARG, "folded buffer must be 256-byte aligned");
+  const size_t need = mla_output_folded_bytes(&c, form);
+  if (folded_bytes < need)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "output fold buffer holds %zu bytes, %zu needed", folded_bytes,
+                need);
+  mla::launch_fold_output(form, w_uv, w_o, folded, c.num_attention_heads, c.kv_lora_rank, c.v_head_dim,
+                          c.d_model, (hipStream_t)hip_stream);
+  const mla_status st = hip_check("output fold launch");
+  if (st != MLA_OK) return st;
+  L->wo_p = folded;
+  L->out_form = form;
+  return MLA_OK;
+}
+
+namespace {
+struct ProjectLayout {
+  size_t off_dec, off_act, off_part, total;
+  int K;
+};
+bool project_layout(const mla_layer* L, int batch, int total_q, int max_q_len, int max_seq_len,
+                    ProjectLayout* pl) {
+  const mla_config& c = L->cfg;
+  const size_t dec = mla_decode_workspace_bytes(L, batch, total_q, max_q_len, max_seq_len, 0);
+  if (dec == 0 || !L->wo_p) return false;
+  pl->K = L->out_form == MLA_OUTPUT_FOLDED ? c.num_attention_heads * c.kv_lora_rank
+                                           : c.num_attention_heads * c.v_head_dim;
+  pl->off_dec = 0;
+  pl->off_act = align256(dec);
+  // unfolded: the per-head outputs [Tq][H*dv]; folded: o_lat sits in the
+  // decode workspace already
+  const size_t act = L->out_form == MLA_OUTPUT_FOLDED ? 0 : (size_t)total_q * pl->K * 2;
+  pl->off_part = pl->off_act + align256(act);
+  pl->total = pl->off_part + align256((size_t)(pl->K / 256) * total_q * c.d_model * 4);
+  return true;
+}
+}  // namespace
+
+size_t mla_decode_project_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_q,
+                                          int32_t max_q_len, int32_t max_seq_len) {
+  if (!L) return 0;
+  ProjectLayout pl;
+  if (!project_layout(L, batch, total_q, max_q_len, max_seq_len, &pl)) return 0;
+  return pl.total;
+}
+
+mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* cu_q, const int32_t* seq_lens,
+                              const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t total_q,
+                              int32_t max_q_len, int32_t max_seq_len, const void* cache, int64_t num_pages,
+                              void* y, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (!L->wo_p) return fail(MLA_ERR_INVALID_ARG, "mla_decode_project: no output projection folded (mla_fold_output)");
+  if (!y || !workspace) return fail(MLA_ERR_INVALID_ARG, "mla_decode_project: null pointer argument");
+  ProjectLayout pl;
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len ||
+      !project_layout(L, batch, total_q, max_q_len, max_seq_len, &pl))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_project: bad sizes");
+  if (workspace_bytes < pl.total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "project workspace holds %zu bytes, %zu needed",
+                workspace_bytes, pl.total);
+  if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const mla_config& c = L->cfg;
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  const size_t dec_bytes = pl.off_act;
+  const void* act;
+  mla_status s;
+  if (L->out_form == MLA_OUTPUT_UNFOLDED) {
+    s = mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, max_seq_len, 0,
+                          cache, num_pages, ws + pl.off_act, ws, dec_bytes, hip_stream, MLA_PHASE_ALL);
+    act = ws + pl.off_act;
+  } else {
+    // absorb and attend as in decode, then the split merge into o_lat (no W_uv)
+    s = mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, max_seq_len, 0,
+                          cache, num_pages, y, ws, dec_bytes, hip_stream, MLA_PHASE_ABSORB | MLA_PHASE_ATTEND);
+    if (s != MLA_OK) return s;
+    mla::SplitPlan p;
+    make_plan(L, batch, max_q_len, max_seq_len, 0, &p);
+    const DecodeLayout d = decode_layout(L, total_q, p);
+    mla::launch_combine(L->elem, p, (const float*)(ws + d.off_opart), (const float*)(ws + d.off_lse), cu_q,
+                        seq_lens, batch, total_q, c.num_attention_heads, c.kv_lora_rank, ws + d.off_olat, st);
+    act = ws + d.off_olat;
+  }
+  if (s != MLA_OK) return s;
+  mla::launch_project(act, L->wo_p, (float*)(ws + pl.off_part), y, total_q, c.d_model, pl.K, st);
+  return hip_check("project launch");
 }
 
 }  // extern "C"

@@ -105,4 +105,14 @@ void launch_extend_attn(const void* q, const void* kexp, const void* vexp, const
                         int page_size, int lmax, const RopeFreq& freq, float scale, void* out,
                         hipStream_t st);
 
+// ---- output projection (bf16 layers) ----------------------------------------
+// form 1: W_o [H*dv][dm] -> tiled (rows j < dm, k < H*dv); form 2: the fold
+// W_uvo[j][h*dc + c] = sum_v W_uv[c][h*dv + v] W_o[h*dv + v][j], tiled (K = H*dc).
+void launch_fold_output(int form, const void* w_uv, const void* w_o, void* out, int H, int dc, int dv,
+                        int dm, hipStream_t st);
+// y[M][N] (bf16) = a[M][K] . W^T for a tiled W (rows N, contraction K), via
+// split-K fp32 partials part[K/256][M][N] summed in split order.
+void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,
+                    hipStream_t st);
+
 }  // namespace mla

@@ -135,7 +135,8 @@ class Workload:
     spare_page_frac: float = 0.0
     description: str = ""
     kind: str = "decode"              # "decode": the step is append + mla_decode;
-                                      # "extend": append + mla_extend (long chunks)
+                                      # "extend": append + mla_extend (long chunks);
+                                      # "project": append + mla_decode_project
     layers: int = 0                   # > 0: a stack of this many layers sharing one
                                       # page-pool table (one timed pass = all layers)
 
@@ -283,6 +284,11 @@ WORKLOADS = {
         prefix_source="hidden", fixed_prefix=8191,
         description="bf16 layer over an FP8 latent cache; Llama-2-7B shape with a 512-wide latent, "
                     "batch 64, every context 8192"),
+    "dsv2_b32_ctx4096_project": Workload(
+        "dsv2_b32_ctx4096_project", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
+        kind="project",
+        description="bf16; DeepSeek-V2 shape, batch 32, every context 4096, q_len 1, decode and the "
+                    "output projection W_o (the value up-projection folded into it or not)"),
     "dsv2_60layers_b32_ctx4096": Workload(
         "dsv2_60layers_b32_ctx4096", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
         layers=60,

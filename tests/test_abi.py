@@ -158,3 +158,20 @@ def test_fp8_cache_format(mla):
     n8 = mla.mla_plan_max_sequences(_cfg(mla, cache_format=1), 60, 80 * GIB, 32768)
     assert n8 == (80 * GIB) // (60 * 32768 * 644)
     assert mla.mla_plan_max_sequences(_cfg(mla), 60, 80 * GIB, 32768) == 37
+
+
+def test_output_form_choice(mla):
+    """Folding W_uv into W_o streams H d_c d_model weights instead of
+    H d_v (d_c + d_model): a loss unless d_model < d_c d_v / (d_c - d_v)."""
+    UNF, FOL = mla.MLA_OUTPUT_UNFOLDED, mla.MLA_OUTPUT_FOLDED
+    dsv2 = _cfg(mla)
+    for tq in (1, 32, 4096):
+        assert mla.mla_output_choose_form(dsv2, tq) == UNF
+    # d_v = d_c: the fold removes a product and streams fewer bytes
+    wide_v = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                  v_head_dim=32, kv_lora_rank=32, dtype=0)
+    assert mla.mla_output_choose_form(wide_v, 1) == FOL
+    assert mla.mla_output_choose_form(dsv2, 0) == -1
+    assert mla.mla_output_folded_bytes(dsv2, UNF) == 128 * 128 * 5120 * 2
+    assert mla.mla_output_folded_bytes(dsv2, FOL) == 128 * 512 * 5120 * 2
+    assert mla.mla_output_folded_bytes(wide_v, UNF) == 0          # fp32: no projection kernels
