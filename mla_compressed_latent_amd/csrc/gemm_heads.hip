@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 //      block issued at once);
 //   2. o_lat rows = sum_s w_s O_s / sum w_s (normalised partials), rounded to
 //      bf16 into LDS; each thread keeps 16 row-split loads of 16 bytes in
-//      flight;
+//      flight, the first 16 issued before step 1's lse loads;
 //   3. out^T = W_uv_h^T . o_lat^T on the matrix core, waves 0..3 taking value
 //      column blocks w, w + 4, ...; the B operand comes from LDS (columns past
 //      TB hold stale values and are never stored).
@@ -229,6 +229,40 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
     sb_s[tid] = sb;
   }
   __syncthreads();
+
+  // This thread's partial rows: the first round of their loads is issued
+  // before the split weights are known, so its latency runs under the lse
+  // loads and the weight computation.
+  constexpr int kRows = TB * (kDc / 4) / kCombThreads;   // rows per thread (TB / 4)
+  constexpr int kSp = 16 / kRows;                        // splits per round of loads
+  const int j = 4 * (tid & 127), r0 = tid >> 7;
+  f32x4 oacc[kRows];
+  const float* src[kRows];
+#pragma unroll
+  for (int u = 0; u < kRows; ++u) {
+    oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t = min(tb * TB + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
+    src[u] = opart + ((int64_t)t * H + h) * kDc + j;
+  }
+  // splits a row's sequence has (the rows of one thread are the same for
+  // the whole wave, so these guards never diverge)
+  int sb[kRows], smax = 0;
+#pragma unroll
+  for (int u = 0; u < kRows; ++u) {
+    sb[u] = sb_s[r0 + 4 * u];
+    smax = max(smax, sb[u]);
+  }
+  f32x4 v[kSp][kRows];
+  auto load_round = [&](int sp0) {
+#pragma unroll
+    for (int d = 0; d < kSp; ++d)
+#pragma unroll
+      for (int u = 0; u < kRows; ++u)
+        if (sp0 + d < sb[u])
+          v[d][u] = *reinterpret_cast<const f32x4*>(src[u] + (sp0 + d) * rows_total * kDc);
+  };
+  load_round(0);
+
   constexpr int kLseTot = kCombineMaxSplits * TB;   // (split, row) pairs
   constexpr int kLsePerThread = (kLseTot + kCombThreads - 1) / kCombThreads;
   {
@@ -262,39 +296,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   __syncthreads();
 
   {
-    constexpr int kRows = TB * (kDc / 4) / kCombThreads;   // rows per thread (TB / 4)
-    constexpr int kSp = 16 / kRows;                        // splits per round of loads
-    const int j = 4 * (tid & 127), r0 = tid >> 7;
-    f32x4 acc[kRows];
-    const float* src[kRows];
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int t = min(tb * TB + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
-      src[u] = opart + ((int64_t)t * H + h) * kDc + j;
-    }
-    // splits a row's sequence has (the rows of one thread are the same for
-    // the whole wave, so these guards never diverge)
-    int sb[kRows], smax = 0;
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      sb[u] = sb_s[r0 + 4 * u];
-      smax = max(smax, sb[u]);
-    }
     for (int sp0 = 0; sp0 < smax; sp0 += kSp) {
-      f32x4 v[kSp][kRows];
-#pragma unroll
-      for (int d = 0; d < kSp; ++d)
-#pragma unroll
-        for (int u = 0; u < kRows; ++u)
-          if (sp0 + d < sb[u])
-            v[d][u] = *reinterpret_cast<const f32x4*>(src[u] + (sp0 + d) * rows_total * kDc);
+      if (sp0 > 0) load_round(sp0);
 #pragma unroll
       for (int d = 0; d < kSp; ++d)
 #pragma unroll
         for (int u = 0; u < kRows; ++u) {
           const float w = (sp0 + d < sb[u]) ? w_s[sp0 + d][r0 + 4 * u] : 0.f;
-          if (w != 0.f) acc[u] += w * v[d][u];
+          if (w != 0.f) oacc[u] += w * v[d][u];
         }
     }
 #pragma unroll
@@ -302,8 +311,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       const int r = r0 + 4 * u;
       const float inv = inv_s[r];
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 o = {from_f32<bf16>(acc[u][0] * inv), from_f32<bf16>(acc[u][1] * inv),
-                  from_f32<bf16>(acc[u][2] * inv), from_f32<bf16>(acc[u][3] * inv)};
+      bf16x4 o = {from_f32<bf16>(oacc[u][0] * inv), from_f32<bf16>(oacc[u][1] * inv),
+                  from_f32<bf16>(oacc[u][2] * inv), from_f32<bf16>(oacc[u][3] * inv)};
       *reinterpret_cast<bf16x4*>(&ob[r][j]) = o;
     }
   }
