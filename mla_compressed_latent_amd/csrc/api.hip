@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
 #include <string>
 
 #include "../../include/mla.h"
@@ -132,11 +133,10 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
     if (kv_chunk % 64 || kv_chunk > 8192) return false;
     p->chunk = kv_chunk;
   } else {
-    // One resident workgroup per compute unit (two when the row block is
-    // small); cover the longest sequences with about one wave of workgroups,
-    // capped so ragged batches still balance.
-    const int per_cu = 1;
-    const double target = (double)L->num_cus * per_cu;
+    // One resident workgroup per compute unit: cover the longest sequences
+    // with about one wave of workgroups, capped so ragged batches still
+    // balance.
+    const double target = (double)L->num_cus;
     const double work = (double)batch * p->RQ * max_seq_len;
     long c = (long)ceil(work / target);
     c = ((c + 63) / 64) * 64;
@@ -262,7 +262,8 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
     return fail(MLA_ERR_HIP, "cannot query the current device");
-  mla_layer* L = new mla_layer;
+  mla_layer* L = new (std::nothrow) mla_layer;
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "mla_fold_weights: out of host memory");
   L->cfg = *cfg;
   L->elem = elem_of(cfg);
   L->scale = cfg->softmax_scale > 0.f
@@ -507,8 +508,13 @@ mla_status mla_fold_output(mla_layer* L, const void* w_uv, const void* w_o, int3
     return fail(MLA_ERR_INVALID_ARG, "mla_fold_output: unknown form %d", form);
   if (c.dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_UNSUPPORTED, "mla_fold_output: the projection kernels need a bf16 layer");
-  if ((c.num_attention_heads * c.v_head_dim) % 256)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_output: num_attention_heads * v_head_dim must be a multiple of 256");
+  // contraction width of the projection GEMM (its k-split is 256 wide)
+  const int64_t K = (int64_t)c.num_attention_heads *
+                    (form == MLA_OUTPUT_FOLDED ? c.kv_lora_rank : c.v_head_dim);
+  if (K % 256)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_fold_output: num_attention_heads * %s must be a multiple of 256",
+                form == MLA_OUTPUT_FOLDED ? "kv_lora_rank" : "v_head_dim");
   if (!w_o || !folded || (form == MLA_OUTPUT_FOLDED && !w_uv))
     return fail(MLA_ERR_INVALID_ARG, "mla_fold_output: null pointer argument");
   if ((uintptr_t)folded % 256) return fail(MLA_ERR_INVALID_ARG, "folded buffer must be 256-byte aligned");

@@ -92,10 +92,15 @@ mla_status mla_pool_create(int64_t num_pages, int32_t page_size, int32_t max_seq
   p->page_size = page_size;
   p->max_seqs = max_seqs;
   p->max_pages_per_seq = max_pages_per_seq;
-  p->free_stack.resize((size_t)num_pages);
-  for (int64_t i = 0; i < num_pages; ++i) p->free_stack[(size_t)i] = (int32_t)(num_pages - 1 - i);
-  p->pages.resize((size_t)max_seqs);
-  p->length.assign((size_t)max_seqs, 0);
+  try {   // no exception crosses the C boundary
+    p->free_stack.resize((size_t)num_pages);
+    for (int64_t i = 0; i < num_pages; ++i) p->free_stack[(size_t)i] = (int32_t)(num_pages - 1 - i);
+    p->pages.resize((size_t)max_seqs);
+    p->length.assign((size_t)max_seqs, 0);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return mla_api::fail_msg(MLA_ERR_INVALID_ARG, "mla_pool_create: out of host memory");
+  }
   *out = p;
   return MLA_OK;
 }
@@ -116,6 +121,11 @@ mla_status mla_pool_reserve(mla_page_pool* p, int32_t seq, int64_t length) {
     if (more > p->free_stack.size())
       return mla_api::fail_msg(MLA_ERR_INSUFFICIENT_WORKSPACE,
                                "mla_pool_reserve: not enough free pages");
+    try {   // grow first, so that a failure leaves the pool unchanged
+      mine.reserve(need);
+    } catch (const std::bad_alloc&) {
+      return mla_api::fail_msg(MLA_ERR_INVALID_ARG, "mla_pool_reserve: out of host memory");
+    }
     for (size_t i = 0; i < more; ++i) {
       mine.push_back(p->free_stack.back());
       p->free_stack.pop_back();
@@ -131,6 +141,7 @@ mla_status mla_pool_release(mla_page_pool* p, int32_t seq) {
     return mla_api::fail_msg(MLA_ERR_INVALID_ARG, "mla_pool_release: sequence id out of range");
   std::vector<int32_t>& mine = p->pages[(size_t)seq];
   // last page first, so that the next reservation gets them back in order
+  // (the stack's capacity is num_pages from creation: no reallocation here)
   for (size_t i = mine.size(); i-- > 0;) p->free_stack.push_back(mine[i]);
   mine.clear();
   p->length[(size_t)seq] = 0;
