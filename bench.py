@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode workloads: time mla_append_latent + mla_decode instead of mla_decode_step")
     ap.add_argument("--path", choices=("auto", "absorbed", "expanded"), default="auto",
                     help="form of mla_extend for extend workloads")
     ap.add_argument("--form", choices=("auto", "unfolded", "folded"), default="auto",
@@ -222,6 +224,8 @@ def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
         st["dws"] = torch.empty(max(1, mla.mla_decode_workspace_bytes(layer0, B, Tq, st["max_q_len"],
                                                                       st["max_seq_len"], kv_chunk)),
                                 dtype=torch.uint8, device=dev)
+        st["sws"] = torch.empty(max(1, mla.mla_decode_step_workspace_bytes(
+            layer0, B, Tq, Tq, st["max_q_len"], st["max_seq_len"], kv_chunk)), dtype=torch.uint8, device=dev)
     return st
 
 
@@ -253,6 +257,12 @@ def run_step(st, i, ev=None, path=None):
                        workspace=st["dws"])
         if ev is not None:
             ev[2].record()
+        return
+    if ev is None and not st["separate"]:
+        # the whole step in one call: the append GEMM and the query absorb share a launch
+        mla.mla_decode_step(layer, st["x_new"], st["cu_q"], st["prefix"], st["q"], st["cu_q"], st["seq_lens"],
+                            st["table"], cache, st["out"], st["max_q_len"], st["max_seq_len"], st["kv_chunk"],
+                            workspace=st["sws"])
         return
     args = (layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["out"], st["max_q_len"],
             st["max_seq_len"], st["kv_chunk"], st["dws"])
@@ -365,6 +375,7 @@ def main():
     torch.cuda.set_device(0)
     log(f"workload {wl.name}: {wl.description}")
     st = build_state(wl, args.kv_chunk, args.rotate, args.path, args.form)
+    st["separate"] = args.separate
     if st["extend"] or st["project"]:
         return main_extend(args, wl, st)
     log(f"kv_chunk {st['chunk']}, {st['R']} rotated copies of cache ({st['cache_bytes'] / 1e6:.1f} MB) "
@@ -480,7 +491,11 @@ def main():
         },
         "latent_cache_GBps": achieved,
         "latent_cache_frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
-        "timing": "HIP graph replay of whole steps (append + decode); one graph holds one step on each of the R rotated layer copies",
+        "timing": ("HIP graph replay of whole steps ("
+                   + ("mla_append_latent + mla_decode" if st["separate"] else
+                      "mla_decode_step: append + decode, the append GEMM and the query absorb in one launch")
+                   + "); one graph holds one step on each of the R rotated layer copies; phase_us and "
+                   "eager_ms_per_step time the separate calls"),
         "ms_per_step_p10_p50_p90": [pct(per_step, 0.1), pct(per_step, 0.5), pct(per_step, 0.9)],
         "mall_warm_ms_per_step": warm_ms_step,
         "end_to_end_latent_GBps": latent_bytes / (ms_step * 1e-3) / 1e9,

@@ -221,6 +221,30 @@ mla_status mla_decode_phases(const mla_layer* layer, const void* q, const int32_
                              void* workspace, size_t workspace_bytes, void* hip_stream,
                              uint32_t phases);
 
+/* A whole decode step of one layer: mla_append_latent of the new tokens'
+ * rows (x, cu_new, prefix_lens, total_new as there) followed by mla_decode
+ * of the queries (q, cu_q, seq_lens, ... as there; seq_lens count the rows
+ * just appended), with the same results bit for bit, in fewer launches: on
+ * bf16 layers the append GEMM and the query absorb, independent of each
+ * other, share one launch ("Multi-head Latent Attention: the KV cache,
+ * compressed": section "Store the archive, not the files" for the latent
+ * x W_dkv that a step caches, section "Absorption: the part that makes it
+ * free" for folding W_uk onto the query; neither product needs the other).
+ *   workspace  device, 256-byte aligned, >= mla_decode_step_workspace_bytes
+ *              (the decode workspace, then the append's)
+ * Errors: those of mla_append_latent and mla_decode; nothing is enqueued
+ * when a host check fails. */
+size_t mla_decode_step_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_new,
+                                       int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                                       int32_t kv_chunk);
+mla_status mla_decode_step(const mla_layer* layer, const void* x, const int32_t* cu_new,
+                           const int32_t* prefix_lens, int32_t total_new, const void* q,
+                           const int32_t* cu_q, const int32_t* seq_lens,
+                           const int32_t* page_table, int32_t max_pages, int32_t batch,
+                           int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                           int32_t kv_chunk, void* cache, int64_t num_pages, void* out,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Prefill and chunked extend: many new query tokens per sequence over the
  * same paged cache ("Multi-head Latent Attention and KV Cache Compression",
  * sections "The absorption trick and decoupled RoPE" and "What separates

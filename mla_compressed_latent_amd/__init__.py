@@ -25,6 +25,7 @@ __all__ = [
     "MlaCachePlan", "mla_plan_cache", "mla_plan_max_sequences", "PagePool", "MLA_CACHE_DTYPE", "MLA_CACHE_FP8",
     "mla_output_choose_form", "mla_output_folded_bytes", "mla_fold_output", "mla_decode_project_workspace_bytes",
     "mla_decode_project", "MLA_OUTPUT_AUTO", "MLA_OUTPUT_UNFOLDED", "MLA_OUTPUT_FOLDED",
+    "mla_decode_step_workspace_bytes", "mla_decode_step",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -43,8 +44,8 @@ EXPORTED_SYMBOLS = (
     "mla_extend_workspace_bytes", "mla_extend", "mla_plan_cache", "mla_plan_max_sequences",
     "mla_pool_create", "mla_pool_destroy", "mla_pool_reserve", "mla_pool_release", "mla_pool_free_pages",
     "mla_pool_length", "mla_pool_page_table", "mla_output_choose_form", "mla_output_folded_bytes",
-    "mla_fold_output", "mla_decode_project_workspace_bytes", "mla_decode_project", "mla_status_string",
-    "mla_last_error",
+    "mla_fold_output", "mla_decode_project_workspace_bytes", "mla_decode_project",
+    "mla_decode_step_workspace_bytes", "mla_decode_step", "mla_status_string", "mla_last_error",
 )
 
 
@@ -111,6 +112,9 @@ def _load():
         "mla_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_decode_phases": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P,
                                     ctypes.c_uint32]),
+        "mla_decode_step_workspace_bytes": (S, [P, I32, I32, I32, I32, I32, I32]),
+        "mla_decode_step": (I32, [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S,
+                                  P]),
         "mla_extend_choose_path": (I32, [cfgp, I32, I32, I32, I32]),
         "mla_extend_workspace_bytes": (S, [P, I32, I32, I32, I32, I32]),
         "mla_extend": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
@@ -296,6 +300,31 @@ def mla_decode_phases(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, m
         int(max_seq_len), int(kv_chunk), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
         int(phases)), "mla_decode")
+
+
+def mla_decode_step_workspace_bytes(layer: Layer, batch: int, total_new: int, total_q: int, max_q_len: int,
+                                    max_seq_len: int, kv_chunk: int = 0) -> int:
+    return int(lib.mla_decode_step_workspace_bytes(layer.handle, batch, total_new, total_q, max_q_len,
+                                                   max_seq_len, kv_chunk))
+
+
+def mla_decode_step(layer: Layer, x, cu_new, prefix_lens, q, cu_q, seq_lens, page_table, cache, out,
+                    max_q_len: int, max_seq_len: int, kv_chunk: int = 0, workspace=None, stream=None):
+    """mla_append_latent of x's rows, then mla_decode of q, in fewer launches (see include/mla.h)."""
+    dt = layer.cfg.torch_dtype
+    total_new, total_q = int(x.shape[0]), int(q.shape[0])
+    batch = int(seq_lens.shape[0])
+    if workspace is None:
+        n = mla_decode_step_workspace_bytes(layer, batch, total_new, total_q, max_q_len, max_seq_len, kv_chunk)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=q.device)
+    _check(lib.mla_decode_step(
+        layer.handle, _dev(x, "x", dt), _dev(cu_new, "cu_new", torch.int32),
+        _dev(prefix_lens, "prefix_lens", torch.int32), total_new, _dev(q, "q", dt),
+        _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
+        int(max_seq_len), int(kv_chunk), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]),
+        _dev(out, "out", dt), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "mla_decode_step")
 
 
 def mla_extend_choose_path(cfg: MlaConfig, batch: int, total_q: int, max_q_len: int, max_seq_len: int) -> int:

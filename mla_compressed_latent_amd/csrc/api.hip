@@ -211,6 +211,86 @@ int choose_extend_path(const mla_config& c, int batch, int total_q, int max_q_le
 
 }  // namespace
 
+namespace {
+
+// Host checks of a decode call; fills the split plan and the workspace layout.
+mla_status decode_prepare(const mla_layer* L, const void* q, const int32_t* cu_q,
+                          const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                          int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                          int32_t kv_chunk, const void* cache, int64_t num_pages, const void* out,
+                          const void* workspace, size_t workspace_bytes, mla::SplitPlan* p,
+                          DecodeLayout* d) {
+  if (!q || !cu_q || !seq_lens || !page_table || !cache || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer argument");
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len || max_pages <= 0 ||
+      num_pages <= 0 || (int64_t)max_pages * L->cfg.page_size < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_decode: bad sizes (batch %d, total_q %d, max_q_len %d, max_seq_len %d, max_pages %d)",
+                batch, total_q, max_q_len, max_seq_len, max_pages);
+  if ((int64_t)total_q > (int64_t)batch * max_q_len)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: total_q exceeds batch * max_q_len");
+  if (kv_chunk < 0 || kv_chunk % 64 || kv_chunk > 8192)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a multiple of 64 up to 8192");
+  if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, p))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: cannot plan the split");
+  *d = decode_layout(L, total_q, *p);
+  if (workspace_bytes < d->total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "decode workspace holds %zu bytes, %zu needed",
+                workspace_bytes, d->total);
+  if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MLA_OK;
+}
+
+// Enqueues the given phases of a decode call that passed decode_prepare.
+void decode_launch(const mla_layer* L, const void* q, const int32_t* cu_q, const int32_t* seq_lens,
+                   const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t total_q,
+                   int32_t max_q_len, const void* cache, void* out, char* ws, const mla::SplitPlan& p,
+                   const DecodeLayout& d, uint32_t phases, hipStream_t st) {
+  const mla_config& c = L->cfg;
+  void* abuf = ws + d.off_abuf;
+  float* opart = (float*)(ws + d.off_opart);
+  float* lse = (float*)(ws + d.off_lse);
+  void* olat = ws + d.off_olat;
+  const int H = c.num_attention_heads;
+  if (phases & MLA_PHASE_ABSORB)
+    mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, max_q_len, H,
+                       c.qk_nope_head_dim, c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, L->freq,
+                       L->scale * 1.4426950408889634f, st);
+  if (phases & MLA_PHASE_ATTEND)
+    mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
+                        c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
+                        c.cache_format == MLA_CACHE_FP8, st);
+  if (phases & MLA_PHASE_OUTPUT) {
+    if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
+      mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
+                              c.v_head_dim, L->num_cus, st);
+    } else {
+      mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank,
+                          olat, st);
+      mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim,
+                           st);
+    }
+  }
+}
+
+// The append's rows from its GEMM partials (part): sum, rotate, round and
+// scatter into the pages (or quantize, for FP8 pages).
+void append_finish(const mla_layer* L, const float* part, const int32_t* cu_new,
+                   const int32_t* prefix_lens, const int32_t* page_table, int32_t max_pages,
+                   int32_t batch, int32_t total_new, void* cache, hipStream_t st) {
+  const mla_config& c = L->cfg;
+  const int ks = L->elem == 2 ? mla::append_ksplits_bf16(c.d_model) : 1;
+  if (c.cache_format == MLA_CACHE_FP8)
+    mla::launch_append_finish_fp8(part, ks, total_new, cu_new, prefix_lens, page_table, max_pages, batch,
+                                  cache, c.page_size, L->freq, st);
+  else
+    mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
+                              batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
+                              L->freq, st);
+}
+
+}  // namespace
+
 // Shared with the host-only parts of the library (pool.cpp).
 namespace mla_api {
 mla_status fail_msg(mla_status s, const char* msg) { return fail(s, "%s", msg); }
@@ -316,20 +396,11 @@ mla_status mla_append_latent(const mla_layer* L, const void* x, const int32_t* c
   const int D = c.kv_lora_rank + c.qk_rope_head_dim;
   hipStream_t st = (hipStream_t)hip_stream;
   float* part = (float*)workspace;
-  int ks = 1;
-  if (L->elem == 2) {
-    ks = mla::append_ksplits_bf16(c.d_model);
+  if (L->elem == 2)
     mla::launch_append_gemm_bf16(x, L->wdkv_t, part, total_new, D, c.d_model, st);
-  } else {
-    mla::launch_append_gemm_f32(x, L->wdkv_t, part, total_new, D, c.d_model, st);
-  }
-  if (c.cache_format == MLA_CACHE_FP8)
-    mla::launch_append_finish_fp8(part, ks, total_new, cu_new, prefix_lens, page_table, max_pages, batch,
-                                  cache, c.page_size, L->freq, st);
   else
-    mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
-                              batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
-                              L->freq, st);
+    mla::launch_append_gemm_f32(x, L->wdkv_t, part, total_new, D, c.d_model, st);
+  append_finish(L, part, cu_new, prefix_lens, page_table, max_pages, batch, total_new, cache, st);
   return hip_check("append launch");
 }
 
@@ -359,52 +430,14 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
   if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
   if (phases == 0 || (phases & ~(uint32_t)MLA_PHASE_ALL))
     return fail(MLA_ERR_INVALID_ARG, "mla_decode_phases: bad phase mask 0x%x", phases);
-  if (!q || !cu_q || !seq_lens || !page_table || !cache || !out || !workspace)
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer argument");
-  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len || max_pages <= 0 ||
-      num_pages <= 0 || (int64_t)max_pages * L->cfg.page_size < max_seq_len)
-    return fail(MLA_ERR_INVALID_ARG,
-                "mla_decode: bad sizes (batch %d, total_q %d, max_q_len %d, max_seq_len %d, max_pages %d)",
-                batch, total_q, max_q_len, max_seq_len, max_pages);
-  if ((int64_t)total_q > (int64_t)batch * max_q_len)
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode: total_q exceeds batch * max_q_len");
-  if (kv_chunk < 0 || kv_chunk % 64 || kv_chunk > 8192)
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a multiple of 64 up to 8192");
   mla::SplitPlan p;
-  if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p))
-    return fail(MLA_ERR_INVALID_ARG, "mla_decode: cannot plan the split");
-  const DecodeLayout d = decode_layout(L, total_q, p);
-  if (workspace_bytes < d.total)
-    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "decode workspace holds %zu bytes, %zu needed",
-                workspace_bytes, d.total);
-  if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const mla_config& c = L->cfg;
-  hipStream_t st = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  void* abuf = ws + d.off_abuf;
-  float* opart = (float*)(ws + d.off_opart);
-  float* lse = (float*)(ws + d.off_lse);
-  void* olat = ws + d.off_olat;
-  const int H = c.num_attention_heads;
-  if (phases & MLA_PHASE_ABSORB)
-    mla::launch_absorb(L->elem, q, L->wuk_p, abuf, cu_q, seq_lens, batch, total_q, max_q_len, H,
-                       c.qk_nope_head_dim, c.qk_rope_head_dim, c.kv_lora_rank, c.rope_base, L->freq,
-                       L->scale * 1.4426950408889634f, st);
-  if (phases & MLA_PHASE_ATTEND)
-    mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
-                        c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
-                        c.cache_format == MLA_CACHE_FP8, st);
-  if (phases & MLA_PHASE_OUTPUT) {
-    if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
-      mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
-                              c.v_head_dim, L->num_cus, st);
-    } else {
-      mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank,
-                          olat, st);
-      mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim,
-                           st);
-    }
-  }
+  DecodeLayout d;
+  const mla_status s = decode_prepare(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                                      max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
+                                      &p, &d);
+  if (s != MLA_OK) return s;
+  decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out,
+                (char*)workspace, p, d, phases, (hipStream_t)hip_stream);
   return hip_check("decode launch");
 }
 
@@ -416,6 +449,59 @@ mla_status mla_decode(const mla_layer* L, const void* q, const int32_t* cu_q, co
   return mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
                            max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
                            hip_stream, MLA_PHASE_ALL);
+}
+
+size_t mla_decode_step_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_new,
+                                       int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                                       int32_t kv_chunk) {
+  if (!L || total_new < 0) return 0;
+  const size_t dec = mla_decode_workspace_bytes(L, batch, total_q, max_q_len, max_seq_len, kv_chunk);
+  if (dec == 0) return 0;
+  return align256(dec) + mla_append_workspace_bytes(L, total_new);
+}
+
+mla_status mla_decode_step(const mla_layer* L, const void* x, const int32_t* cu_new,
+                           const int32_t* prefix_lens, int32_t total_new, const void* q,
+                           const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
+                           int32_t max_pages, int32_t batch, int32_t total_q, int32_t max_q_len,
+                           int32_t max_seq_len, int32_t kv_chunk, void* cache, int64_t num_pages,
+                           void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (total_new < 0) return fail(MLA_ERR_INVALID_ARG, "mla_decode_step: total_new %d < 0", total_new);
+  if (total_new > 0 && (!x || !cu_new || !prefix_lens))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_step: null pointer argument");
+  mla::SplitPlan p;
+  DecodeLayout d;
+  mla_status s = decode_prepare(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                                max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes, &p,
+                                &d);
+  if (s != MLA_OK) return s;
+  const size_t off_app = align256(d.total);
+  const size_t need = off_app + mla_append_workspace_bytes(L, total_new);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "decode step workspace holds %zu bytes, %zu needed",
+                workspace_bytes, need);
+  const mla_config& c = L->cfg;
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  float* part = (float*)(ws + off_app);
+  const int D = c.kv_lora_rank + c.qk_rope_head_dim;
+  uint32_t phases = MLA_PHASE_ALL;
+  if (total_new > 0) {
+    if (L->elem == 2) {
+      mla::launch_absorb_append(q, L->wuk_p, ws + d.off_abuf, cu_q, seq_lens, batch, total_q, max_q_len,
+                                c.num_attention_heads, c.qk_nope_head_dim, c.qk_rope_head_dim,
+                                c.kv_lora_rank, L->freq, L->scale * 1.4426950408889634f, x, L->wdkv_t, part,
+                                total_new, D, c.d_model, st);
+      phases = MLA_PHASE_ATTEND | MLA_PHASE_OUTPUT;
+    } else {
+      mla::launch_append_gemm_f32(x, L->wdkv_t, part, total_new, D, c.d_model, st);
+    }
+    append_finish(L, part, cu_new, prefix_lens, page_table, max_pages, batch, total_new, cache, st);
+  }
+  decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p, d,
+                phases, st);
+  return hip_check("decode step launch");
 }
 
 int32_t mla_extend_choose_path(const mla_config* cfg, int32_t batch, int32_t total_q, int32_t max_q_len,

@@ -10,43 +10,19 @@
 // The GEMM is split along d_model so that a handful of new tokens still
 // spreads over the whole chip; the split partials are summed in a fixed
 // order by the finishing kernel, so the cache contents are deterministic.
+#include "append_gemm.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mla {
 namespace {
 
-constexpr int kAppendKChunk = 256;   // d_model elements per split
-
-// One wave: u^T block (32 row elements x 32 tokens) over one k chunk, the
-// folded W_dkv as the A operand (contiguous fragments), the hidden states as
-// the B operand.  Each lane stores 4 consecutive row elements of one token.
+// One wave per (32-token block, 32 row elements, k chunk).
 __global__ __launch_bounds__(64) void append_gemm_bf16_kernel(const bf16* __restrict__ x,
                                                               const bf16* __restrict__ wdkv,
                                                               float* __restrict__ part, int M,
                                                               int N, int K) {
-  constexpr int NS = kAppendKChunk / 16;
-  const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.x * 32, nb = blockIdx.y, ks = blockIdx.z;
-  const int t = m0 + l32;
-  const bf16* xr = x + (int64_t)min(t, M - 1) * K + ks * kAppendKChunk + 8 * g;
-  bf16x8 a[NS], b[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    a[s] = load_fragment(wdkv, nb, ks * NS + s, K, lane);
-    b[s] = load_bf16x8(xr + 16 * s);
-  }
-  f32x16 acc = zero_f32x16();
-#pragma unroll
-  for (int s = 0; s < NS; ++s) acc = mfma32(a[s], b[s], acc);
-  if (t < M) {
-    float* out = part + ((int64_t)ks * M + t) * N + nb * 32 + 4 * g;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 v = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-      *reinterpret_cast<f32x4*>(out + 8 * r4) = v;
-    }
-  }
+  append_gemm_block(x, wdkv, part, M, N, K, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // fp32 layers: one thread per output element, sequential k order.

@@ -12,6 +12,7 @@
 // Latent Attention: the KV cache, compressed", section "The code",
 // decoupled_score) and appended, giving one d_c + d_rope row per (token, head)
 // that is scored against whole cached rows.
+#include "append_gemm.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,16 +52,16 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float 
 // heads), so each angle is computed once and applied to every head of the
 // block.  Lane l handles pair l % 32 (d_rope = 64) for heads of parity l / 32.
 template <int NS, int JB>   // d_nope / 16, 32-column blocks per wave (held in registers)
-__global__ __launch_bounds__(64) void absorb_bf16_kernel(
+__device__ __forceinline__ void absorb_block(
     const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
-    int dc, int gemm_blocks, int TC, const RopeFreq freq, float qscale) {
+    int dc, int gemm_blocks, int TC, const RopeFreq& freq, float qscale, int bid) {
   constexpr int dn = NS * 16;
-  const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
-  if ((int)blockIdx.x >= gemm_blocks) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
+  if (bid >= gemm_blocks) {
     const int p = l32, hpar = g;
     const int HG = (H + kRopeHeads - 1) / kRopeHeads;
-    const int rid = blockIdx.x - gemm_blocks;
+    const int rid = bid - gemm_blocks;
     const int hg = rid % HG, tc = (rid / HG) % TC, b = rid / (HG * TC);
     const int q0 = cu_q[b], Lq = cu_q[b + 1] - q0, L = seq_lens[b];
     const int dq = dn + dr, D = dc + dr;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(64) void absorb_bf16_kernel(
   const int JG = dc / 32 / JB;
   const int ntb = (Tq + 31) / 32;
   const int TBW = min(ntb, kAbsorbTokBlocks);   // token blocks per wave
-  const int id = blockIdx.x;
+  const int id = bid;
   const int jg = id % JG, h = (id / JG) % H, tbg = id / (JG * H);
   const int dq = dn + dr, D = dc + dr;
   const bf16* wh = wuk + (int64_t)h * dc * dn;
@@ -132,6 +133,36 @@ __global__ __launch_bounds__(64) void absorb_bf16_kernel(
       compute(tb + 1, qb);
     }
   }
+}
+
+template <int NS, int JB>
+__global__ __launch_bounds__(64) void absorb_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
+    int dc, int gemm_blocks, int TC, const RopeFreq freq, float qscale) {
+  absorb_block<NS, JB>(q, wuk, abuf, cu_q, seq_lens, Tq, H, dr, dc, gemm_blocks, TC, freq, qscale,
+                       blockIdx.x);
+}
+
+// A decode step's two independent weight-streaming GEMMs in one launch: the
+// append GEMM of the new tokens' rows (blocks [0, app_blocks), token blocks
+// fastest, then row-element blocks, then k chunks) and the query absorb with
+// its rope rotation (the rest).  Both are one-wave blocks; the absorb, the
+// longer of the two, hides the append behind it.
+template <int NS, int JB>
+__global__ __launch_bounds__(64) void absorb_append_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
+    int dc, int gemm_blocks, int TC, const RopeFreq freq, float qscale, const bf16* __restrict__ x,
+    const bf16* __restrict__ wdkv, float* __restrict__ part, int M, int N, int K, int app_blocks) {
+  const int bid = blockIdx.x;
+  if (bid < app_blocks) {
+    const int MB = (M + 31) / 32, NB = N / 32;
+    append_gemm_block(x, wdkv, part, M, N, K, bid % MB, (bid / MB) % NB, bid / (MB * NB));
+    return;
+  }
+  absorb_block<NS, JB>(q, wuk, abuf, cu_q, seq_lens, Tq, H, dr, dc, gemm_blocks, TC, freq, qscale,
+                       bid - app_blocks);
 }
 
 // out^T block = W_uv_h^T (32 value rows x d_c) . o_lat^T (d_c x 32 tokens).
@@ -398,20 +429,59 @@ __global__ void out_proj_f32_kernel(const float* __restrict__ olat, const float*
 
 }  // namespace
 
+namespace {
+// Grid of the bf16 absorb: GEMM waves, then rope workgroups.
+struct AbsorbGrid {
+  int jb;            // 32-column weight blocks per wave
+  int gemm_blocks;   // GEMM waves
+  int TC;            // rope workgroups per sequence and head block
+  int blocks;        // total
+};
+AbsorbGrid absorb_grid(int batch, int Tq, int max_q_len, int H, int dn, int dc) {
+  AbsorbGrid a;
+  const int ntb = (Tq + 31) / 32;
+  const int tbw = ntb < kAbsorbTokBlocks ? ntb : kAbsorbTokBlocks;
+  // weight blocks per wave: 4 (2 when d_nope > 128) amortise the weight
+  // registers over many token blocks
+  a.jb = dn / 16 <= 8 ? 4 : 2;
+  a.gemm_blocks = ((ntb + tbw - 1) / tbw) * H * (dc / 32 / a.jb);
+  a.TC = (max_q_len + kRopeTok - 1) / kRopeTok;
+  const int HG = (H + kRopeHeads - 1) / kRopeHeads;
+  a.blocks = a.gemm_blocks + batch * a.TC * HG;
+  return a;
+}
+}  // namespace
+
+void launch_absorb_append(const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                          const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn,
+                          int dr, int dc, const RopeFreq& freq, float qscale, const void* x,
+                          const void* wdkv, float* part, int M, int N, int K, hipStream_t st) {
+  const AbsorbGrid a = absorb_grid(batch, Tq, max_q_len, H, dn, dc);
+  const int gemm_blocks = a.gemm_blocks, TC = a.TC;
+  const int app_blocks = ((M + 31) / 32) * (N / 32) * (K / kAppendKChunk);
+  const unsigned blocks = (unsigned)(app_blocks + a.blocks);
+  switch (dn / 16 * 8 + a.jb) {
+#define MLA_FUSED_CASE(NS, JB)                                                                     \
+  case NS * 8 + JB:                                                                                \
+    absorb_append_bf16_kernel<NS, JB><<<blocks, 64, 0, st>>>(                                      \
+        (const bf16*)q, (const bf16*)wuk, (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, gemm_blocks, \
+        TC, freq, qscale, (const bf16*)x, (const bf16*)wdkv, part, M, N, K, app_blocks);           \
+    break;
+    MLA_FUSED_CASE(2, 4) MLA_FUSED_CASE(4, 4) MLA_FUSED_CASE(6, 4) MLA_FUSED_CASE(8, 4)
+    MLA_FUSED_CASE(10, 2) MLA_FUSED_CASE(12, 2) MLA_FUSED_CASE(14, 2) MLA_FUSED_CASE(16, 2)
+#undef MLA_FUSED_CASE
+    default: break;   // excluded by the config check
+  }
+}
+
 void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
                    const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
                    int dc, float base, const RopeFreq& freq, float qscale, hipStream_t st) {
   if (elem == 2) {
-    const int ntb = (Tq + 31) / 32;
-    const int tbw = ntb < kAbsorbTokBlocks ? ntb : kAbsorbTokBlocks;
-    // weight blocks per wave: 4 (2 when d_nope > 128) amortise the weight
-    // registers over many token blocks
-    const int jb = dn / 16 <= 8 ? 4 : 2;
-    const int gemm_blocks = ((ntb + tbw - 1) / tbw) * H * (dc / 32 / jb);
-    const int TC = (max_q_len + kRopeTok - 1) / kRopeTok;
-    const int HG = (H + kRopeHeads - 1) / kRopeHeads;
-    const unsigned blocks = (unsigned)(gemm_blocks + batch * TC * HG);
-    switch (dn / 16 * 8 + jb) {
+    const AbsorbGrid a = absorb_grid(batch, Tq, max_q_len, H, dn, dc);
+    const int gemm_blocks = a.gemm_blocks, TC = a.TC;
+    const unsigned blocks = (unsigned)a.blocks;
+    switch (dn / 16 * 8 + a.jb) {
 #define MLA_ABSORB_CASE(NS, JB)                                                                    \
   case NS * 8 + JB:                                                                                \
     absorb_bf16_kernel<NS, JB><<<blocks, 64, 0, st>>>((const bf16*)q, (const bf16*)wuk,           \

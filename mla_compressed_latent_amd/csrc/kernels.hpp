@@ -48,6 +48,12 @@ void launch_append_finish_fp8(const float* part, int ksplits, int T, const int32
 void launch_absorb(int elem, const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
                    const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn, int dr,
                    int dc, float base, const RopeFreq& freq, float qscale, hipStream_t st);
+// bf16 layers: launch_absorb's work and launch_append_gemm_bf16's (part,
+// M = new tokens, N = row width, K = d_model) as one launch of one-wave blocks.
+void launch_absorb_append(const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                          const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn,
+                          int dr, int dc, const RopeFreq& freq, float qscale, const void* x,
+                          const void* wdkv, float* part, int M, int N, int K, hipStream_t st);
 // out[t][h][v] = sum_j olat[t][h][j] * wuv_p[h][v][j]
 void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
                      int dv, hipStream_t st);
