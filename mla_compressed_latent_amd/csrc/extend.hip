@@ -14,10 +14,11 @@
 // kernels, both on the matrix cores, every operand streamed HBM -> LDS as
 // whole 1 KB MFMA fragments by the LDS-DMA path:
 //
-//  expand_kv_kernel   one workgroup per (sequence, head, 256 tokens):
-//                     K_h = C W_uk_h and V_h = C W_uv_h, stored per 64-token
-//                     tile as the attention kernel's operand fragments, so
-//                     its copies are contiguous 1 KB reads.
+//  expand_kv_kernel   one workgroup per (sequence, group of heads, 256
+//                     tokens): K_h = C W_uk_h and V_h = C W_uv_h for each
+//                     head of the group in turn, stored per 64-token tile as
+//                     the attention kernel's operand fragments, so its
+//                     copies are contiguous 1 KB reads.
 //  extend_attn_kernel one workgroup per (sequence, head, 256 queries), one
 //                     wave per 32 queries: causal flash attention.  Scores
 //                     are formed transposed (S^T = K Q^T, tokens down the
@@ -82,21 +83,26 @@ struct ExpandDims {
 // Both operands are d_c-contiguous, so the two products use the same
 // fragments with the roles of A and B swapped.  Two waves share each SIMD,
 // so one wave's waits and stores overlap the other's matrix work.
+// The nh heads of a workgroup run back to back through one copy pipeline of
+// nh * 16 stages: the next head's first stages are in flight while the
+// current one finishes, its stores overlap the next head's products, and
+// the head's cache-row stages come from L2 (the previous head read them).
 template <int DN, int DV>
 __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
     const bf16* __restrict__ cache, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ page_table, int max_pages, int batch, int H, int page_size,
+    const int32_t* __restrict__ page_table, int max_pages, int batch, int H, int nh, int page_size,
     int lmax, const bf16* __restrict__ wukt, const bf16* __restrict__ wuv,
     bf16* __restrict__ kexp, bf16* __restrict__ vexp) {
   using Dm = ExpandDims<DN, DV>;
   __shared__ __attribute__((aligned(1024))) bf16 sbuf[kExpBuf][Dm::kSlots * 512];
 
   const int ntt = lmax / kExpTok;
-  const int nblocks = batch * H * ntt;
+  const int HG = H / nh;
+  const int nblocks = batch * HG * ntt;
   const int logical = xcd_logical_block(blockIdx.x, nblocks);
   const int tt = logical % ntt;
-  const int h = (logical / ntt) % H;
-  const int b = logical / (ntt * H);
+  const int h = ((logical / ntt) % HG) * nh;   // first head of the group
+  const int b = logical / (ntt * HG);
   const int L = seq_lens[b];
   const int t0 = tt * kExpTok;
   if (t0 >= L) return;
@@ -106,14 +112,17 @@ __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
   const uint32_t lds0 = lds_address(&sbuf[0][0]);
 
-  // Sources of this wave's fragment copies; stage st adds st * stride bytes.
+  // Sources of this wave's fragment copies; stage st of head h + k adds
+  // st * stride + k * head_step bytes.
   const char* src[Dm::kDma];
   uint32_t voff[Dm::kDma];
   uint32_t stride[Dm::kDma];
+  uint32_t head_step[Dm::kDma];
 #pragma unroll
   for (int u = 0; u < Dm::kDma; ++u) {
     int f = wave * Dm::kDma + u;
     if (f >= Dm::kFrag) f = 0;
+    head_step[u] = 0;   // cache rows: the same for every head
     if (f < Dm::kFragC) {
       // slot f: tokens t0 + 16 f .. + 15 (one page: pages hold a multiple of
       // 64 tokens), the stage's 64 bytes of each row as four 16-byte chunks,
@@ -133,32 +142,38 @@ __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
                                              ((int64_t)ib * (kDC / 16) + s) * 512);
       voff[u] = (uint32_t)(lane * 16);
       stride[u] = 2 * 512 * 2;
+      head_step[u] = DN * kDC * 2;
     } else {
       const int g = f - Dm::kFragC - Dm::kFragK, vb = g >> 1, s = g & 1;
       src[u] = reinterpret_cast<const char*>(wuv + (int64_t)h * DV * kDC +
                                              ((int64_t)vb * (kDC / 16) + s) * 512);
       voff[u] = (uint32_t)(lane * 16);
       stride[u] = 2 * 512 * 2;
+      head_step[u] = DV * kDC * 2;
     }
   }
-  auto issue = [&](int st) {
-    const uint32_t dst = lds0 + (uint32_t)(((st % kExpBuf) * Dm::kSlots + wave * Dm::kDma) * 1024);
+  // global stage g = 16 k + st: stage st of head h + k
+  const int nstages = nh * kExpStages;
+  auto issue = [&](int g) {
+    const int k = g / kExpStages, st = g % kExpStages;
+    const uint32_t dst = lds0 + (uint32_t)(((g % kExpBuf) * Dm::kSlots + wave * Dm::kDma) * 1024);
 #pragma unroll
-    for (int u = 0; u < Dm::kDma; ++u) dma16(src[u] + st * stride[u], voff[u], dst + u * 1024);
+    for (int u = 0; u < Dm::kDma; ++u)
+      dma16(src[u] + (int64_t)k * head_step[u] + st * stride[u], voff[u], dst + u * 1024);
   };
-  // stage st is in LDS for every wave, and every wave has finished reading
-  // stage st - 1 (whose buffer the copies issued next overwrite)
-  auto stage_ready = [&](int st) -> const bf16x8* {
-    wait_dma_ahead(min(kExpBuf - 2, kExpStages - 1 - st), Dm::kDma);
+  // stage g is in LDS for every wave, and every wave has finished reading
+  // stage g - 1 (whose buffer the copies issued next overwrite)
+  auto stage_ready = [&](int g) -> const bf16x8* {
+    wait_dma_ahead(min(kExpBuf - 2, nstages - 1 - g), Dm::kDma);
     wait_lds();
     __syncthreads();
-    if (st + kExpBuf - 1 < kExpStages) issue(st + kExpBuf - 1);
-    return reinterpret_cast<const bf16x8*>(&sbuf[st % kExpBuf][0]);
+    if (g + kExpBuf - 1 < nstages) issue(g + kExpBuf - 1);
+    return reinterpret_cast<const bf16x8*>(&sbuf[g % kExpBuf][0]);
   };
 
 #pragma unroll
-  for (int st = 0; st < kExpBuf - 1; ++st) issue(st);
-  const int64_t bh = (int64_t)b * H + h;
+  for (int g = 0; g < kExpBuf - 1; ++g)
+    if (g < nstages) issue(g);
   const int th = wave & 3;
   // cache-row operand of row block j: row r = 64 th + 32 j + l32 of the tile,
   // chunk c at 16-byte position 4 r + (c ^ ((r >> 2) & 3)) -- sixteen
@@ -168,13 +183,15 @@ __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
   const int tile0 = (t0 >> 6) + th;   // this wave's 64-token tile
 
   if (wave < 4) {
+   for (int k = 0; k < nh; ++k) {
+    const int64_t bh = (int64_t)b * H + h + k;
     f32x16 acc[DN / 32][2];
 #pragma unroll
     for (int i = 0; i < DN / 32; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = zero_f32x16();
     for (int st = 0; st < kExpStages; ++st) {
-      const bf16x8* fr = stage_ready(st);
+      const bf16x8* fr = stage_ready(k * kExpStages + st);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         bf16x8 c[2];
@@ -206,14 +223,17 @@ __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
           *reinterpret_cast<bf16x4*>(tb + ((2 * i + (q >> 1)) * 64 + l32 + 32 * (q & 1)) * 8 + 4 * hh) = v;
         }
       }
+   }
   } else {
+   for (int k = 0; k < nh; ++k) {
+    const int64_t bh = (int64_t)b * H + h + k;
     f32x16 acc[2][DV / 32];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < DV / 32; ++i) acc[j][i] = zero_f32x16();
     for (int st = 0; st < kExpStages; ++st) {
-      const bf16x8* fr = stage_ready(st);
+      const bf16x8* fr = stage_ready(k * kExpStages + st);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         bf16x8 c[2];
@@ -247,6 +267,7 @@ __global__ __launch_bounds__(512, 1) void expand_kv_kernel(
           *reinterpret_cast<bf16x8*>(dst + g * 512) = v;
         }
       }
+   }
   }
 }
 
@@ -466,9 +487,11 @@ template <int DN, int DV>
 void expand_for(const void* cache, const int32_t* seq_lens, const int32_t* page_table, int max_pages,
                 int batch, int H, int page_size, int lmax, const void* wukt, const void* wuv,
                 void* kexp, void* vexp, hipStream_t st) {
-  const int nblocks = batch * H * (lmax / kExpTok);
+  // heads per workgroup: four when they divide H, else two, else one
+  const int nh = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
+  const int nblocks = batch * (H / nh) * (lmax / kExpTok);
   expand_kv_kernel<DN, DV><<<nblocks, 64 * kExpWaves, 0, st>>>(
-      (const bf16*)cache, seq_lens, page_table, max_pages, batch, H, page_size, lmax,
+      (const bf16*)cache, seq_lens, page_table, max_pages, batch, H, nh, page_size, lmax,
       (const bf16*)wukt, (const bf16*)wuv, (bf16*)kexp, (bf16*)vexp);
 }
 

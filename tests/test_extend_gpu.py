@@ -79,6 +79,19 @@ def test_prefill_empty_prefix(path):
         _check_all(case, out, f"prefill {q_len} {PATH_NAME[path]}")
 
 
+@pytest.mark.parametrize("H", [2, 6, 8])
+def test_expanded_head_groups(H):
+    """The expansion runs a workgroup's group of heads (four when they divide
+    H, else two, else one) through one copy pipeline: head counts giving
+    groups of two (2, 6) and two groups of four (8), ragged and paged."""
+    wl = workload("dsv2_ragged_paged_256", name=f"ext_heads{H}", shape=_shape(128, 128, H=H), batch=3,
+                  max_prefix=300, max_q_len=300, seed=15)
+    case = _case(wl)
+    out = case.extend(EXP)
+    torch.cuda.synchronize()
+    _check_all(case, out, f"expanded H={H}")
+
+
 def test_expanded_single_queries_and_one_token():
     """Degenerate extends on the expanded path: one query per sequence, and a
     sequence whose whole context is its one query."""
