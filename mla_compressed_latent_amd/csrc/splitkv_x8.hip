@@ -28,8 +28,9 @@
 //
 // F8 (MLA_CACHE_FP8 pages): three bf16 tiles and two FP8 staging buffers; the
 // value waves copy each FP8 tile to staging one tile ahead and, besides their
-// value product for tile it-1, convert tile it+1 (a quarter each) while the
-// score waves use tile it.  Score and value waves run separate loops with the same
+// value product for tile it-1, convert a quarter of tile it+1's latent codes
+// and its rope keys; the score waves convert the other three quarters after
+// their softmax (the value waves' chain is the longer one).  Score and value waves run separate loops with the same
 // barrier sequence, so their operands (query, O) can share the AGPR file.
 #include "attn_tile.hpp"
 #include "common.hpp"
@@ -190,9 +191,9 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       m_run = m_new;
       if (G == 0) alpha_s[it & 1][16 * wave + c16] = alpha;
       if constexpr (F8)
-        if (it + 1 < ntiles)   // latent items 512..1023 of the next tile (value waves: the rest)
-          f8_convert<2>(&stage[(it + 1) & 1][0], reinterpret_cast<char*>(&tiles[(it + 1) % kBuf][0]),
-                        tok_end - (tok_begin + (it + 1) * kTileTok), 512 + 64 * wave + lane, 256,
+        if (it + 1 < ntiles)   // latent items 256..1023 of the next tile (value waves: the rest)
+          f8_convert<3>(&stage[(it + 1) & 1][0], reinterpret_cast<char*>(&tiles[(it + 1) % kBuf][0]),
+                        tok_end - (tok_begin + (it + 1) * kTileTok), 256 + 64 * wave + lane, 256,
                         kTileTok * 32, 256);
     }
     if (G == 0) lrow_s[16 * wave + c16] = l_run;
@@ -238,12 +239,12 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
               dst + kF8RowsBytes);
     };
-    // tile 0 (prologue): all latent items; later tiles: items 0..511 and the
-    // rope items (the score waves convert 512..1023)
+    // tile 0 (prologue): all latent items; later tiles: items 0..255 and the
+    // rope items (the score waves convert 256..1023)
     auto f8_convert_tile = [&](int it) {
       f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
                     tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256,
-                    it == 0 ? kTileTok * 32 : 512, 0);
+                    it == 0 ? kTileTok * 32 : 256, 0);
     };
     // value operand (transposing read, natural token order): in 16-lane group
     // G, source lane 4 j + q points at dims 4q..4q+3 of the group's 16 dims,
