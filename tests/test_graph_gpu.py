@@ -114,3 +114,45 @@ def test_two_stream_graph_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
     print("[graph] 3 two-stream replays identical to eager", flush=True)
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """mla_decode_step (the append GEMM and the query absorb in one launch)
+    captured as a graph: three replays, with eager steps between them, each
+    bit-identical to the eager call."""
+    wl = workload("dsv2_ragged_paged_256", name="graph_step", batch=4, max_prefix=250)
+    print(f"[graph] case {wl.name} B={wl.batch}", flush=True)
+    case = GpuCase(wl)
+    mla = case.mla
+    s = wl.shape
+    Tq = case.q.shape[0]
+    ws = torch.empty(mla.mla_decode_step_workspace_bytes(case.layer, wl.batch, Tq, Tq, case.max_q_len,
+                                                         case.max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def step(out):
+        mla.mla_decode_step(case.layer, case.x_new_dev, case.cu_q, case.prefix_dev, case.q_dev, case.cu_q,
+                            case.seq_lens, case.page_table, case.cache, out, case.max_q_len, case.max_seq_len,
+                            workspace=ws)
+
+    eager = torch.empty((Tq, s.H, s.d_v), dtype=case.dt, device="cuda")
+    step(eager)
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(out_g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    other = torch.empty_like(eager)
+    for rep in range(3):
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), f"decode step graph replay {rep} differs from the eager result"
+        step(other)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    print("[graph] decode step: 3 replays identical to eager", flush=True)
