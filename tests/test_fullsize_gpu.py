@@ -1,8 +1,9 @@
-"""GPU parity at the full sizes of every workload, in the launch
-configuration bench.py times (the library's own split choice): the whole
-batch is appended and decoded on the GPU, and sampled (sequence, head)
-outputs are compared with the float64 oracle computed one sequence at a
-time.  Tolerances as in test_parity_gpu.py."""
+"""GPU parity at the full sizes of every decode workload, in the launch
+configuration bench.py times (one mla_decode_step per layer, the library's
+own split choice): the whole batch is appended and decoded on the GPU, and
+sampled (sequence, head) outputs are compared with the float64 oracle
+computed one sequence at a time (for FP8 pages, over the oracle's own
+quantized rows).  Tolerances as in test_parity_gpu.py."""
 import time
 
 import numpy as np
@@ -33,16 +34,19 @@ def _sampled(name):
 
 
 @pytest.mark.parametrize("name", ["dsv2_b32_ctx4096", "llama2_7b_mla_b64_ctx8192", "dsv2_b8_ctx131072",
-                                  "dsv2_ragged_paged_256"])
+                                  "dsv2_ragged_paged_256", "dsv2_b32_ctx4096_fp8",
+                                  "llama2_7b_mla_b64_ctx8192_fp8"])
 def test_full_size_sampled(name):
     wl, seqs, heads = _sampled(name)
     t0 = time.time()
     print(f"\n[full] {name}: B={wl.batch}, max context {int(wl.seq_lens().max())}, building the cache",
           flush=True)
     case = GpuCase(wl, fill_sentinel=False)
-    print(f"[full] {name}: cache built in {time.time() - t0:.0f}s; append + decode", flush=True)
-    case.append_new()
-    out = case.decode(kv_chunk=0)
+    print(f"[full] {name}: cache built in {time.time() - t0:.0f}s; decode step", flush=True)
+    s = wl.shape
+    out = torch.empty((case.q.shape[0], s.H, s.d_v), dtype=case.dt, device="cuda")
+    case.mla.mla_decode_step(case.layer, case.x_new_dev, case.cu_q, case.prefix_dev, case.q_dev, case.cu_q,
+                             case.seq_lens, case.page_table, case.cache, out, case.max_q_len, case.max_seq_len)
     torch.cuda.synchronize()
     chunk = case.mla.mla_decode_kv_chunk(case.layer, wl.batch, case.max_q_len, case.max_seq_len, 0)
     got = out.float().cpu().numpy()
