@@ -13,6 +13,7 @@
 // decoupled_score) and appended, giving one d_c + d_rope row per (token, head)
 // that is scored against whole cached rows.
 #include "append_gemm.hpp"
+#include "attn_tile.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -216,7 +217,10 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 //      flight, the first 16 issued before step 1's lse loads;
 //   3. out^T = W_uv_h^T . o_lat^T on the matrix core, waves 0..3 taking value
 //      column blocks w, w + 4, ...; the B operand comes from LDS (columns past
-//      TB hold stale values and are never stored).
+//      TB hold stale values and are never stored).  The A operand of a wave's
+//      first block: k-steps 0..15 loaded into registers at the start, 16..31
+//      copied HBM -> LDS at the start by wave w + 4 (otherwise idle then), so
+//      the matrix loop waits on no global load.
 // Splits past a row's sequence were never written: their weight is zero and
 // their (arbitrary) values are never added.
 constexpr int kCombThreads = 512;
@@ -234,6 +238,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   __shared__ float inv_s[TB];
   __shared__ int sb_s[TB];
   __shared__ __attribute__((aligned(16))) bf16 ob[32][kDc + kCombRowPad];
+  constexpr int kGrp = 8;
+  __shared__ __attribute__((aligned(1024))) bf16 wsec[4][2 * kGrp * 512];   // 16 fragments per wave
   const int32_t* cu = stage_cu(cu_st, cu_q, batch);
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H, tb = blockIdx.x / H;
@@ -242,7 +248,6 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
 
   // W_uv fragments of the first value-column block of waves 0..3, loaded
   // first so that their latency hides under the combine
-  constexpr int kGrp = 8;
   const bf16* wh = wuv + (int64_t)h * dv * kDc;
   bf16x8 a[2][kGrp];
   if (wave < 4 && wave < dv / 32) {
@@ -251,6 +256,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       a[0][u] = load_fragment(wh, wave, u, kDc, lane);
       a[1][u] = load_fragment(wh, wave, kGrp + u, kDc, lane);
     }
+  }
+  const int wsel = __builtin_amdgcn_readfirstlane(wave - 4);
+  const bool copies_half = wave >= 4 && wsel < dv / 32;
+  if (copies_half) {
+    const uint32_t dst = lds_address(&wsec[wsel][0]);
+#pragma unroll
+    for (int u = 0; u < 2 * kGrp; ++u)
+      dma16(wh + ((int64_t)wsel * (kDc / 16) + 2 * kGrp + u) * 64 * 8, (uint32_t)lane * 16u, dst + u * 1024);
   }
 
   if (tid < TB) {
@@ -347,6 +360,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       *reinterpret_cast<bf16x4*>(&ob[r][j]) = o;
     }
   }
+  if (copies_half) wait_vmcnt<0>();   // the copied half-block is in LDS
   __syncthreads();
 
   if (wave >= 4) return;
@@ -370,8 +384,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
         acc = mfma32(a[grp & 1][u], bo, acc);
       }
       if (grp + 2 < NS / kGrp) {
+        if (vb == wave) {   // k-steps 16..31 of the first block: from LDS
 #pragma unroll
-        for (int u = 0; u < kGrp; ++u) a[grp & 1][u] = load_fragment(wh, vb, (grp + 2) * kGrp + u, kDc, lane);
+          for (int u = 0; u < kGrp; ++u)
+            a[grp & 1][u] = *reinterpret_cast<const bf16x8*>(&wsec[wave][((grp * kGrp + u) * 64 + lane) * 8]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kGrp; ++u)
+            a[grp & 1][u] = load_fragment(wh, vb, (grp + 2) * kGrp + u, kDc, lane);
+        }
       }
     }
     if (l32 < TB && t < Tq) {
