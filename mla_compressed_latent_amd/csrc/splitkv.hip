@@ -16,8 +16,9 @@
 // go to the eight-wave kernel of splitkv_x8.hip), one workgroup of 4 waves per
 // (sequence, split):
 //   * 32-token tiles of cached rows are copied HBM -> LDS by the LDS-DMA path
-//     (global_load_lds, 16 bytes per lane, every wave copies 8 rows), three
-//     tiles in flight; 16-byte chunks are swizzled per row (swz) so that both
+//     (global_load_lds, 16 bytes per lane, every wave copies 8 rows) into a
+//     ring of four: two in use (the value waves' and the score wave's), two
+//     in flight; 16-byte chunks are swizzled per row (swz) so that both
 //     operand reads below are free of bank conflicts;
 //   * the score wave (0) keeps the 32 rows of the score operand (32 x 576
 //     bf16) in registers and computes S^T = tile . A^T on the 32x32x16 bf16
@@ -36,14 +37,15 @@
 namespace mla {
 namespace {
 
-constexpr int kNBuf = 4;                      // tiles resident in LDS (3 in flight)
+constexpr int kNBuf = 4;                      // tiles resident in LDS (2 in use, 2 in flight)
 constexpr int kQkRing = 3;                    // score-operand read groups in flight
 constexpr int kPvRing = 6;                    // value-operand reads in flight
 
 // F8: MLA_CACHE_FP8 pages.  Waves 1-3 copy each FP8 tile to one of two
 // staging buffers (seven 1 KB copies each) and convert it into the bf16 tile
-// ring (three tiles), a third each, while the score wave scores the tile
-// before it and the value waves use the one before that.
+// ring (three tiles) -- wave 1, which has no matrix work, half the latent
+// codes and all rope keys, the value waves a quarter each -- while the score
+// wave scores the tile before it and the value waves use the one before that.
 template <int NB, bool F8>
 __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const bf16* __restrict__ abuf, const void* __restrict__ cache_v, const int32_t* __restrict__ cu_q,
