@@ -37,11 +37,11 @@ EXTEND_METRIC = "MLA chunked-extend / prefill query tokens/s and matrix-core TFL
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("4df1e4b2c223f723", "dsv2_b32_ctx4096"): {"fetch_bytes": 155908821, "write_bytes": 36444453},
-    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606556281, "write_bytes": 16893515},
-    ("4df1e4b2c223f723", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210443863, "write_bytes": 72203113},
-    ("4df1e4b2c223f723", "dsv2_b32_ctx4096_fp8"): {"fetch_bytes": 89394526, "write_bytes": 37442013},
-    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192_fp8"): {"fetch_bytes": 340411086, "write_bytes": 17012617},
+    ("4df1e4b2c223f723", "dsv2_b32_ctx4096"): {"fetch_bytes": 155909588, "write_bytes": 36660335},
+    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606559264, "write_bytes": 16882790},
+    ("4df1e4b2c223f723", "dsv2_b8_ctx131072"): {"fetch_bytes": 1209267458, "write_bytes": 35948877},
+    ("4df1e4b2c223f723", "dsv2_b32_ctx4096_fp8"): {"fetch_bytes": 89394731, "write_bytes": 37450015},
+    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192_fp8"): {"fetch_bytes": 340412813, "write_bytes": 17065448},
 }
 
 
@@ -52,9 +52,9 @@ EXTEND_SOURCES = ("attn_tile.hpp", "extend.hip")
 # HBM bytes of one mla_extend call (both expanded kernels), measured as above.
 EXTEND_TRAFFIC = {
     ("0008695d329dc1fc", "dsv2_extend_b4_p3072_c1024"): {
-        "fetch_bytes": 2566137094, "write_bytes": 1207989638,
-        "per_kernel": {"expand_kv": {"fetch_bytes": 1254324129, "write_bytes": 1073741824},
-                       "extend_attn": {"fetch_bytes": 1311812965, "write_bytes": 134247814}}},
+        "fetch_bytes": 2558964580, "write_bytes": 1207988858,
+        "per_kernel": {"expand_kv": {"fetch_bytes": 1247159164, "write_bytes": 1073741824},
+                       "extend_attn": {"fetch_bytes": 1311805416, "write_bytes": 134247034}}},
 }
 
 
