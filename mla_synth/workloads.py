@@ -32,6 +32,7 @@ STREAM_QLEN = 6
 STREAM_PAGES = 7
 STREAM_Q = 8
 STREAM_W_O = 9
+STREAM_W_Q = 10
 
 
 # ---------------------------------------------------------------- bf16 I/O --
@@ -196,6 +197,13 @@ class Workload:
         """Output projection [H * d_v][d_model]: concatenated heads -> hidden size."""
         s = self.shape
         return self._normal(self.rng(STREAM_W_O), (s.H * s.d_v, s.d_model), 1.0 / np.sqrt(s.H * s.d_v))
+
+    def w_q(self) -> np.ndarray:
+        """Query projection [d_model][H * (d_nope + d_rope)]: head h owns the
+        columns h*(d_nope + d_rope) .., its content part first."""
+        s = self.shape
+        return self._normal(self.rng(STREAM_W_Q), (s.d_model, s.H * (s.d_nope + s.d_rope)),
+                            1.0 / np.sqrt(s.d_model))
 
     # ------------------------------------------------------------ activations
     def prefix_hidden(self, b: int) -> np.ndarray:

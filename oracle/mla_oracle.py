@@ -41,6 +41,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * Sequence b holds L_b cached rows after the new tokens are appended; its
   q_len_b queries sit at positions L_b - q_len_b + i and each attends to
   every position not after its own.
+* Where queries are asked for from the layer's input, they are
+  ``x . W_q`` with W_q of shape [d_model][H * (d_nope + d_rope)], head h
+  owning the columns h * (d_nope + d_rope) .., content part first
+  (``project_query``).
 * Output per query and head is ``sum_t w_t V_h[t]`` (no output projection);
   where a layer output is asked for, it is the concatenated heads times an
   output projection W_o of shape [H * d_v][d_model] (``project_output``).
@@ -58,6 +62,7 @@ __all__ = [
     "decode",
     "default_scale",
     "project_output",
+    "project_query",
 ]
 
 
@@ -174,3 +179,16 @@ def project_output(out: np.ndarray, w_o: np.ndarray) -> np.ndarray:
     out = np.asarray(out, dtype=np.float64)
     tq, h, dv = out.shape
     return out.reshape(tq, h * dv) @ np.asarray(w_o, dtype=np.float64)
+
+
+def project_query(x: np.ndarray, w_q: np.ndarray, n_heads: int) -> np.ndarray:
+    """Queries from the layer's input: q[t] = x[t] . W_q, split per head, for
+    x [Tq][d_model] and W_q [d_model][H * (d_nope + d_rope)] ("Multi-head
+    Latent Attention: the KV cache, compressed", section "Store the archive,
+    not the files": the query is a plain linear map of the token's hidden
+    state, into which the key up-projection can be folded once at load).
+    Returns [Tq][H][d_nope + d_rope]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_q = np.asarray(w_q, dtype=np.float64)
+    tq = x.shape[0]
+    return (x @ w_q).reshape(tq, n_heads, w_q.shape[1] // n_heads)
