@@ -423,6 +423,64 @@ mla_status mla_decode_project(const mla_layer* layer, const void* q, const int32
                               const void* cache, int64_t num_pages, void* y, void* workspace,
                               size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Queries from the layer input, with the key up-projection kept apart or
+ * folded into the query projection ("Multi-head Latent Attention: the KV
+ * cache, compressed", section "Store the archive, not the files": the score
+ * (x W_q)(c W_uk)^T equals x (W_q W_uk^T) c^T, so W_abs = W_q W_uk^T is formed
+ * once at load and no key is ever built).
+ *   MLA_QUERY_UNFOLDED  q = x . W_q, then mla_decode's own absorb
+ *                       (weights H*(d_nope + d_rope)*d_model + H*d_nope*d_c elements)
+ *   MLA_QUERY_FOLDED    per head [q_lat | q_rope] = x . [W_q_h^nope W_uk_h^T | W_q_h^rope],
+ *                       folded once at load (H*(d_c + d_rope)*d_model elements)
+ *   MLA_QUERY_AUTO      mla_query_choose_form(cfg, 1)
+ * bf16 layers.  x is whatever the query projection reads (the token's hidden
+ * state, width d_model).
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  MLA_QUERY_AUTO = 0,
+  MLA_QUERY_UNFOLDED = 1,
+  MLA_QUERY_FOLDED = 2
+} mla_query_form;
+
+/* The form with the smaller estimated time for total_q query tokens, each
+ * form's time the larger of its weight bytes / 8 TB/s and its matrix-core
+ * flops / 2.5 PFLOP/s.  Both scale with the weight element counts, so
+ * folding wins when d_model < d_c d_nope / (d_c - d_nope): at d_model 256 for
+ * d_nope >= 192 (d_c 512), never for d_nope 128.  Host only; -1 on an
+ * invalid config or total_q < 1. */
+int32_t mla_query_choose_form(const mla_config* cfg, int32_t total_q);
+
+/* Bytes of the buffer mla_fold_query fills for a form (0 if unsupported). */
+size_t mla_query_folded_bytes(const mla_config* cfg, int32_t form);
+
+/* Attach the query projection to a layer.
+ *   w_q   [d_model][H * (d_nope + d_rope)]  device; head h owns the columns
+ *                              h*(d_nope + d_rope) .., content part first
+ *   w_uk  [d_c][H * d_nope]    device, the same W_uk given to mla_fold_weights
+ *                              (read for MLA_QUERY_FOLDED only; may be null otherwise)
+ *   folded                     device, >= mla_query_folded_bytes(cfg, form),
+ *                              256-byte aligned, kept and read by later calls
+ * The inputs are read by work enqueued on hip_stream.  Errors: INVALID_ARG,
+ * UNSUPPORTED (fp32 layer), INSUFFICIENT_WORKSPACE, HIP. */
+mla_status mla_fold_query(mla_layer* layer, const void* w_q, const void* w_uk, int32_t form,
+                          void* folded, size_t folded_bytes, void* hip_stream);
+
+size_t mla_decode_hidden_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
+                                         int32_t max_q_len, int32_t max_seq_len);
+
+/* mla_decode (kv_chunk 0) with its queries projected from the layer input:
+ * x [total_q][d_model] (bf16) in the token order of cu_q, projected by the
+ * form the layer was folded with (mla_fold_query); out [total_q][H][d_v] as
+ * mla_decode.  Same arguments and contract as mla_decode otherwise; the
+ * workspace is scratch for this call only.  Errors as mla_decode, and
+ * INVALID_ARG when no query projection was folded. */
+mla_status mla_decode_hidden(const mla_layer* layer, const void* x, const int32_t* cu_q,
+                             const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                             int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                             const void* cache, int64_t num_pages, void* out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 

@@ -26,6 +26,8 @@ __all__ = [
     "mla_output_choose_form", "mla_output_folded_bytes", "mla_fold_output", "mla_decode_project_workspace_bytes",
     "mla_decode_project", "MLA_OUTPUT_AUTO", "MLA_OUTPUT_UNFOLDED", "MLA_OUTPUT_FOLDED",
     "mla_decode_step_workspace_bytes", "mla_decode_step",
+    "mla_query_choose_form", "mla_query_folded_bytes", "mla_fold_query", "mla_decode_hidden_workspace_bytes",
+    "mla_decode_hidden", "MLA_QUERY_AUTO", "MLA_QUERY_UNFOLDED", "MLA_QUERY_FOLDED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -36,6 +38,7 @@ MLA_PHASE_ABSORB, MLA_PHASE_ATTEND, MLA_PHASE_OUTPUT, MLA_PHASE_ALL = 1, 2, 4, 7
 MLA_EXTEND_AUTO, MLA_EXTEND_ABSORBED, MLA_EXTEND_EXPANDED = 0, 1, 2
 MLA_CACHE_DTYPE, MLA_CACHE_FP8 = 0, 1
 MLA_OUTPUT_AUTO, MLA_OUTPUT_UNFOLDED, MLA_OUTPUT_FOLDED = 0, 1, 2
+MLA_QUERY_AUTO, MLA_QUERY_UNFOLDED, MLA_QUERY_FOLDED = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
@@ -45,7 +48,9 @@ EXPORTED_SYMBOLS = (
     "mla_pool_create", "mla_pool_destroy", "mla_pool_reserve", "mla_pool_release", "mla_pool_free_pages",
     "mla_pool_length", "mla_pool_page_table", "mla_output_choose_form", "mla_output_folded_bytes",
     "mla_fold_output", "mla_decode_project_workspace_bytes", "mla_decode_project",
-    "mla_decode_step_workspace_bytes", "mla_decode_step", "mla_status_string", "mla_last_error",
+    "mla_decode_step_workspace_bytes", "mla_decode_step", "mla_query_choose_form", "mla_query_folded_bytes",
+    "mla_fold_query", "mla_decode_hidden_workspace_bytes", "mla_decode_hidden", "mla_status_string",
+    "mla_last_error",
 )
 
 
@@ -132,6 +137,11 @@ def _load():
         "mla_fold_output": (I32, [P, P, P, I32, P, S, P]),
         "mla_decode_project_workspace_bytes": (S, [P, I32, I32, I32, I32]),
         "mla_decode_project": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
+        "mla_query_choose_form": (I32, [cfgp, I32]),
+        "mla_query_folded_bytes": (S, [cfgp, I32]),
+        "mla_fold_query": (I32, [P, P, P, I32, P, S, P]),
+        "mla_decode_hidden_workspace_bytes": (S, [P, I32, I32, I32, I32]),
+        "mla_decode_hidden": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error": (ctypes.c_char_p, []),
     }
@@ -429,6 +439,53 @@ def mla_fold_output(layer: Layer, w_uv, w_o, form: int = MLA_OUTPUT_AUTO, folded
     layer.out_folded = folded     # the layer reads it from now on
     layer.out_form = form
     return form
+
+
+def mla_query_choose_form(cfg: MlaConfig, total_q: int) -> int:
+    return int(lib.mla_query_choose_form(ctypes.byref(cfg), int(total_q)))
+
+
+def mla_query_folded_bytes(cfg: MlaConfig, form: int) -> int:
+    return int(lib.mla_query_folded_bytes(ctypes.byref(cfg), int(form)))
+
+
+def mla_fold_query(layer: Layer, w_q, w_uk, form: int = MLA_QUERY_AUTO, folded=None, stream=None):
+    """Attach the query projection (W_q, or W_q_h W_uk_h^T folded) to the layer."""
+    dt = layer.cfg.torch_dtype
+    if form == MLA_QUERY_AUTO:
+        form = mla_query_choose_form(layer.cfg, 1)
+    n = mla_query_folded_bytes(layer.cfg, form)
+    if folded is None:
+        folded = torch.empty(max(1, n), dtype=torch.uint8, device=w_q.device)
+    _check(lib.mla_fold_query(layer.handle, _dev(w_q, "w_q", dt), None if w_uk is None else _dev(w_uk, "w_uk", dt),
+                              int(form), _dev(folded, "folded"), folded.numel(), _stream(stream)),
+           "mla_fold_query")
+    layer.q_folded = folded       # the layer reads it from now on
+    layer.q_form = form
+    return form
+
+
+def mla_decode_hidden_workspace_bytes(layer: Layer, batch: int, total_q: int, max_q_len: int,
+                                      max_seq_len: int) -> int:
+    return int(lib.mla_decode_hidden_workspace_bytes(layer.handle, batch, total_q, max_q_len, max_seq_len))
+
+
+def mla_decode_hidden(layer: Layer, x, cu_q, seq_lens, page_table, cache, out, max_q_len: int, max_seq_len: int,
+                      workspace=None, stream=None):
+    """Decode with the queries projected from the layer input x [total_q][d_model]."""
+    dt = layer.cfg.torch_dtype
+    total_q = int(x.shape[0])
+    batch = int(seq_lens.shape[0])
+    if workspace is None:
+        n = mla_decode_hidden_workspace_bytes(layer, batch, total_q, max_q_len, max_seq_len)
+        workspace = torch.empty(max(1, n), dtype=torch.uint8, device=x.device)
+    _check(lib.mla_decode_hidden(
+        layer.handle, _dev(x, "x", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), batch, total_q, int(max_q_len),
+        int(max_seq_len), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]),
+        _dev(out, "out", dt), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)),
+        "mla_decode_hidden")
 
 
 def mla_decode_project_workspace_bytes(layer: Layer, batch: int, total_q: int, max_q_len: int,

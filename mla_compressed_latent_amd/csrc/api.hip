@@ -25,6 +25,8 @@ struct mla_layer {
   int num_cus;
   void* wo_p = nullptr;  // output projection, tiled (mla_fold_output)
   int out_form = 0;      // MLA_OUTPUT_UNFOLDED or MLA_OUTPUT_FOLDED once folded
+  void* wq_p = nullptr;  // query projection, tiled (mla_fold_query)
+  int q_form = 0;        // MLA_QUERY_UNFOLDED or MLA_QUERY_FOLDED once folded
 };
 
 namespace {
@@ -690,6 +692,128 @@ mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* 
   if (s != MLA_OK) return s;
   mla::launch_project(act, L->wo_p, (float*)(ws + pl.off_part), y, total_q, c.d_model, pl.K, st);
   return hip_check("project launch");
+}
+
+int32_t mla_query_choose_form(const mla_config* cfg, int32_t total_q) {
+  if (check_config(cfg) != MLA_OK || total_q < 1) return -1;
+  // weight bytes streamed and matrix-core flops of the two forms (the
+  // unfolded form also runs the per-head absorb through W_uk)
+  const double H = cfg->num_attention_heads, dc = cfg->kv_lora_rank, dn = cfg->qk_nope_head_dim;
+  const double dr = cfg->qk_rope_head_dim, dm = cfg->d_model;
+  const double e = cfg->dtype == MLA_DTYPE_BF16 ? 2.0 : 4.0, T = total_q;
+  const double wu = H * ((dn + dr) * dm + dn * dc), wf = H * (dc + dr) * dm;
+  const double unf = fmax(e * wu / 8e12, 2.0 * T * wu / 2.5e15);
+  const double fol = fmax(e * wf / 8e12, 2.0 * T * wf / 2.5e15);
+  return fol < unf ? MLA_QUERY_FOLDED : MLA_QUERY_UNFOLDED;
+}
+
+size_t mla_query_folded_bytes(const mla_config* cfg, int32_t form) {
+  if (check_config(cfg) != MLA_OK || cfg->dtype != MLA_DTYPE_BF16) return 0;
+  const size_t H = cfg->num_attention_heads, dm = cfg->d_model;
+  if (form == MLA_QUERY_UNFOLDED) return align256(H * (cfg->qk_nope_head_dim + cfg->qk_rope_head_dim) * dm * 2);
+  if (form == MLA_QUERY_FOLDED) return align256(H * (cfg->kv_lora_rank + cfg->qk_rope_head_dim) * dm * 2);
+  return 0;
+}
+
+mla_status mla_fold_query(mla_layer* L, const void* w_q, const void* w_uk, int32_t form, void* folded,
+                          size_t folded_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  const mla_config& c = L->cfg;
+  if (form == MLA_QUERY_AUTO) form = mla_query_choose_form(&c, 1);
+  if (form != MLA_QUERY_UNFOLDED && form != MLA_QUERY_FOLDED)
+    return fail(MLA_ERR_INVALID_ARG, "mla_fold_query: unknown form %d", form);
+  if (c.dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_query: the projection kernels need a bf16 layer");
+  if (!w_q || !folded || (form == MLA_QUERY_FOLDED && !w_uk))
+    return fail(MLA_ERR_INVALID_ARG, "mla_fold_query: null pointer argument");
+  if ((uintptr_t)folded % 256) return fail(MLA_ERR_INVALID_ARG, "folded buffer must be 256-byte aligned");
+  const size_t need = mla_query_folded_bytes(&c, form);
+  if (folded_bytes < need)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "query fold buffer holds %zu bytes, %zu needed", folded_bytes,
+                need);
+  mla::launch_fold_query(form, w_q, w_uk, folded, c.num_attention_heads, c.qk_nope_head_dim,
+                         c.qk_rope_head_dim, c.kv_lora_rank, c.d_model, (hipStream_t)hip_stream);
+  const mla_status st = hip_check("query fold launch");
+  if (st != MLA_OK) return st;
+  L->wq_p = folded;
+  L->q_form = form;
+  return MLA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// Workspace of mla_decode_hidden: the decode's own, then (unfolded form) the
+// projected queries [Tq][H*dq], then the projection's split-K partials.
+struct HiddenLayout {
+  size_t off_q, off_part, total;
+  int N;
+};
+bool hidden_layout(const mla_layer* L, int batch, int total_q, int max_q_len, int max_seq_len,
+                   HiddenLayout* hl) {
+  const mla_config& c = L->cfg;
+  const size_t dec = mla_decode_workspace_bytes(L, batch, total_q, max_q_len, max_seq_len, 0);
+  if (dec == 0 || !L->wq_p) return false;
+  const bool folded = L->q_form == MLA_QUERY_FOLDED;
+  hl->N = c.num_attention_heads *
+          ((folded ? c.kv_lora_rank : c.qk_nope_head_dim) + c.qk_rope_head_dim);
+  hl->off_q = align256(dec);
+  hl->off_part = hl->off_q + (folded ? 0 : align256((size_t)total_q * hl->N * 2));
+  hl->total = hl->off_part +
+              align256((size_t)mla::append_ksplits_bf16(c.d_model) * total_q * hl->N * 4);
+  return true;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_hidden_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_q,
+                                         int32_t max_q_len, int32_t max_seq_len) {
+  if (!L) return 0;
+  HiddenLayout hl;
+  if (!hidden_layout(L, batch, total_q, max_q_len, max_seq_len, &hl)) return 0;
+  return hl.total;
+}
+
+mla_status mla_decode_hidden(const mla_layer* L, const void* x, const int32_t* cu_q, const int32_t* seq_lens,
+                             const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t total_q,
+                             int32_t max_q_len, int32_t max_seq_len, const void* cache, int64_t num_pages,
+                             void* out, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (!L->wq_p) return fail(MLA_ERR_INVALID_ARG, "mla_decode_hidden: no query projection folded (mla_fold_query)");
+  HiddenLayout hl;
+  if (batch <= 0 || total_q < batch || max_q_len <= 0 || max_seq_len < max_q_len ||
+      !hidden_layout(L, batch, total_q, max_q_len, max_seq_len, &hl))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_hidden: bad sizes");
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "mla_decode_hidden: null pointer argument");
+  if (workspace_bytes < hl.total)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "hidden-input decode workspace holds %zu bytes, %zu needed",
+                workspace_bytes, hl.total);
+  const mla_config& c = L->cfg;
+  hipStream_t st = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  float* part = (float*)(ws + hl.off_part);
+  mla::SplitPlan p;
+  DecodeLayout d;
+  const mla_status s = decode_prepare(L, x, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                                      max_seq_len, 0, cache, num_pages, out, ws, hl.off_q, &p, &d);
+  if (s != MLA_OK) return s;
+  if (L->q_form == MLA_QUERY_UNFOLDED) {
+    // q = x . W_q, then the whole decode from q (its own absorb)
+    void* q = ws + hl.off_q;
+    mla::launch_project(x, L->wq_p, part, q, total_q, hl.N, c.d_model, st);
+    decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p, d,
+                  MLA_PHASE_ALL, st);
+  } else {
+    // folded: the projection writes the attention's query rows directly
+    mla::launch_append_gemm_bf16(x, L->wq_p, part, total_q, hl.N, c.d_model, st);
+    mla::launch_query_finish(part, mla::append_ksplits_bf16(c.d_model), total_q, c.num_attention_heads,
+                             c.kv_lora_rank, c.qk_rope_head_dim, cu_q, seq_lens, batch, L->freq,
+                             L->scale * 1.4426950408889634f, ws + d.off_abuf, st);
+    decode_launch(L, x, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p,
+                  d, MLA_PHASE_ATTEND | MLA_PHASE_OUTPUT, st);
+  }
+  return hip_check("hidden-input decode launch");
 }
 
 }  // extern "C"

@@ -116,6 +116,16 @@ void launch_extend_attn(const void* q, const void* kexp, const void* vexp, const
 // W_uvo[j][h*dc + c] = sum_v W_uv[c][h*dv + v] W_o[h*dv + v][j], tiled (K = H*dc).
 void launch_fold_output(int form, const void* w_uv, const void* w_o, void* out, int H, int dc, int dv,
                         int dm, hipStream_t st);
+// ---- queries from the layer input (bf16 layers) -------------------------------
+// form 1: W_q [dm][H*dq] -> tiled (rows H*dq, k < dm); form 2: the fold
+// W_qa[h*D + j] = [W_q_h^nope W_uk_h^T | W_q_h^rope] (D = dc + dr), tiled (k < dm).
+void launch_fold_query(int form, const void* w_q, const void* w_uk, void* out, int H, int dn, int dr,
+                       int dc, int dm, hipStream_t st);
+// abuf[t][h][:] (the attention's query rows, times qscale, rope part rotated at
+// the token's position) from the split-K partials part[ks][Tq][H*(dc + dr)].
+void launch_query_finish(const float* part, int ks, int Tq, int H, int dc, int dr, const int32_t* cu_q,
+                         const int32_t* seq_lens, int batch, const RopeFreq& freq, float qscale, void* abuf,
+                         hipStream_t st);
 // y[M][N] (bf16) = a[M][K] . W^T for a tiled W (rows N, contraction K), via
 // split-K fp32 partials part[K/256][M][N] summed in split order.
 void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,

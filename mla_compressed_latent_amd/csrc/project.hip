@@ -11,20 +11,99 @@
 // stored fragment-tiled at load (rows = the d_model outputs, contraction
 // index k), run by the split-K matrix-core GEMM of the append path and a
 // fixed-order reduction of its fp32 partials.
+//
+// The queries themselves can come from the layer input the same way, with
+// the key up-projection kept apart or folded into the query projection
+// ("Multi-head Latent Attention: the KV cache, compressed", section "Store
+// the archive, not the files": (x W_q)(c W_uk)^T = x (W_q W_uk^T) c^T, so
+// W_abs = W_q W_uk^T is formed once at load):
+//
+//   unfolded:  q = x . W_q, then the decode's own absorb      N = H * (d_nope + d_rope)
+//   folded:    [q_lat | q_rope]_h = x . [W_q_h^nope W_uk_h^T | W_q_h^rope]
+//              straight into the attention's query rows         N = H * (d_c + d_rope)
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mla {
 namespace {
 
-// W_o [H*dv][dm] -> tiled rows j < dm, k = h*dv + v.  One thread per element.
-__global__ void pack_wo_kernel(const bf16* __restrict__ w_o, bf16* __restrict__ out, int K, int dm) {
-  const int64_t n = (int64_t)K * dm;
+// Row-major W [K][N] -> tiled rows j < N, contraction k < K (W_o with K =
+// H*dv, N = dm; W_q with K = dm, N = H*(dn + dr)).  One thread per element.
+__global__ void pack_tiled_kernel(const bf16* __restrict__ w, bf16* __restrict__ out, int K, int N) {
+  const int64_t n = (int64_t)K * N;
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
        o += (int64_t)gridDim.x * blockDim.x) {
-    const int j = (int)(o % dm), k = (int)(o / dm);   // consecutive threads: consecutive j
-    out[tiled_index(j, k, K)] = w_o[(int64_t)k * dm + j];
+    const int j = (int)(o % N), k = (int)(o / N);   // consecutive threads: consecutive j
+    out[tiled_index(j, k, K)] = w[(int64_t)k * N + j];
   }
+}
+
+// W_qa rows r = h*D + j (D = dc + dr), contraction k < dm, stored tiled:
+//   j <  dc: sum_i W_q[k][h*dq + i] W_uk[j][h*dn + i]  (fp32 in i order, rounded to bf16)
+//   j >= dc: W_q[k][h*dq + dn + j - dc]                (the rope columns, copied)
+// with dq = dn + dr.  One thread per element; a one-time fold at load.
+__global__ void fold_wqa_kernel(const bf16* __restrict__ w_q, const bf16* __restrict__ w_uk,
+                                bf16* __restrict__ out, int H, int dn, int dr, int dc, int dm) {
+  const int D = dc + dr, dq = dn + dr;
+  const int64_t n = (int64_t)H * D * dm;
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int k = (int)(o % dm), r = (int)(o / dm);   // consecutive threads: consecutive k
+    const int h = r / D, j = r % D;
+    const bf16* a = w_q + (int64_t)k * H * dq + (int64_t)h * dq;
+    bf16 v;
+    if (j < dc) {
+      const bf16* b = w_uk + (int64_t)j * H * dn + (int64_t)h * dn;
+      float acc = 0.f;
+      for (int i = 0; i < dn; ++i) acc = fmaf(to_f32(a[i]), to_f32(b[i]), acc);
+      v = from_f32<bf16>(acc);
+    } else {
+      v = a[dn + j - dc];
+    }
+    out[tiled_index(r, k, dm)] = v;
+  }
+}
+
+// The attention's query rows abuf[t][h][0 : D] from the split-K partials of
+// x . W_qa (part[s][t][h*D + j]): the splits summed in order, the content
+// part multiplied by qscale, each rope pair (2p, 2p+1) rotated by the
+// token's position times theta_p and then multiplied by qscale -- the same
+// rows the absorb kernel writes from an unfolded query.  One thread per
+// (token, head, element pair).
+__global__ void query_finish_kernel(const float* __restrict__ part, int ks, int Tq, int H, int dc,
+                                    int dr, const int32_t* __restrict__ cu_q,
+                                    const int32_t* __restrict__ seq_lens, int batch, RopeFreq freq,
+                                    float qscale, bf16* __restrict__ abuf) {
+  const int D = dc + dr, P = D / 2;
+  const int64_t n = (int64_t)Tq * H * P;
+  const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n) return;
+  const int p = (int)(o % P);
+  const int64_t th = o / P;   // t * H + h
+  const int t = (int)(th / H);
+  const int64_t e = th * D + 2 * p;
+  const int64_t stride = (int64_t)Tq * H * D;
+  float x0 = 0.f, x1 = 0.f;
+  for (int s = 0; s < ks; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(part + s * stride + e);
+    x0 += v.x;
+    x1 += v.y;
+  }
+  float y0, y1;
+  if (2 * p < dc) {
+    y0 = x0 * qscale;
+    y1 = x1 * qscale;
+  } else {
+    const int b = seq_of_token(cu_q, batch, t);
+    const int pos = seq_lens[b] - (cu_q[b + 1] - cu_q[b]) + (t - cu_q[b]);
+    float c, sn;
+    rope_cos_sin_reduced(pos, freq.theta[p - dc / 2], &c, &sn);
+    y0 = (x0 * c - x1 * sn) * qscale;
+    y1 = (x0 * sn + x1 * c) * qscale;
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r = {from_f32<bf16>(y0), from_f32<bf16>(y1)};
+  *reinterpret_cast<bf16x2*>(abuf + e) = r;
 }
 
 // W_uvo[j][h*dc + c] = sum_v W_uv[c][h*dv + v] W_o[h*dv + v][j], fp32
@@ -62,9 +141,26 @@ __global__ void sum_splits_kernel(const float* __restrict__ part, int ks, int M,
 void launch_fold_output(int form, const void* w_uv, const void* w_o, void* out, int H, int dc, int dv,
                         int dm, hipStream_t st) {
   if (form == 1)
-    pack_wo_kernel<<<4096, 256, 0, st>>>((const bf16*)w_o, (bf16*)out, H * dv, dm);
+    pack_tiled_kernel<<<4096, 256, 0, st>>>((const bf16*)w_o, (bf16*)out, H * dv, dm);
   else
     fold_wuvo_kernel<<<8192, 256, 0, st>>>((const bf16*)w_uv, (const bf16*)w_o, (bf16*)out, H, dc, dv, dm);
+}
+
+void launch_fold_query(int form, const void* w_q, const void* w_uk, void* out, int H, int dn, int dr,
+                       int dc, int dm, hipStream_t st) {
+  if (form == 1)
+    pack_tiled_kernel<<<4096, 256, 0, st>>>((const bf16*)w_q, (bf16*)out, dm, H * (dn + dr));
+  else
+    fold_wqa_kernel<<<8192, 256, 0, st>>>((const bf16*)w_q, (const bf16*)w_uk, (bf16*)out, H, dn, dr, dc,
+                                          dm);
+}
+
+void launch_query_finish(const float* part, int ks, int Tq, int H, int dc, int dr, const int32_t* cu_q,
+                         const int32_t* seq_lens, int batch, const RopeFreq& freq, float qscale, void* abuf,
+                         hipStream_t st) {
+  const int64_t n = (int64_t)Tq * H * ((dc + dr) / 2);
+  query_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, ks, Tq, H, dc, dr, cu_q, seq_lens,
+                                                                   batch, freq, qscale, (bf16*)abuf);
 }
 
 void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,

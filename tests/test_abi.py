@@ -175,3 +175,24 @@ def test_output_form_choice(mla):
     assert mla.mla_output_folded_bytes(dsv2, UNF) == 128 * 128 * 5120 * 2
     assert mla.mla_output_folded_bytes(dsv2, FOL) == 128 * 512 * 5120 * 2
     assert mla.mla_output_folded_bytes(wide_v, UNF) == 0          # fp32: no projection kernels
+
+
+def test_query_form_choice(mla):
+    """Folding W_uk into the query projection streams H (d_c + d_rope) d_model
+    weights instead of H ((d_nope + d_rope) d_model + d_nope d_c): a loss
+    unless d_model < d_c d_nope / (d_c - d_nope)."""
+    UNF, FOL = mla.MLA_QUERY_UNFOLDED, mla.MLA_QUERY_FOLDED
+    dsv2 = _cfg(mla)
+    for tq in (1, 32, 4096):
+        assert mla.mla_query_choose_form(dsv2, tq) == UNF
+    # d_nope 192, d_model 256: 256 < 512 * 192 / 320 = 307.2, the fold wins
+    narrow = _cfg(mla, d_model=256, num_attention_heads=16, qk_nope_head_dim=192)
+    assert mla.mla_query_choose_form(narrow, 1) == FOL
+    # d_nope 128, d_model 256: 256 > 512 * 128 / 384 = 170.7
+    assert mla.mla_query_choose_form(_cfg(mla, d_model=256, num_attention_heads=16), 1) == UNF
+    assert mla.mla_query_choose_form(dsv2, 0) == -1
+    assert mla.mla_query_folded_bytes(dsv2, UNF) == 128 * 192 * 5120 * 2
+    assert mla.mla_query_folded_bytes(dsv2, FOL) == 128 * 576 * 5120 * 2
+    fp32 = _cfg(mla, d_model=64, num_attention_heads=4, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                v_head_dim=16, kv_lora_rank=32, dtype=0)
+    assert mla.mla_query_folded_bytes(fp32, FOL) == 0          # fp32: no projection kernels

@@ -160,3 +160,22 @@ def test_many_splits_separate_combine():
     out_fused = case.decode(kv_chunk=128)     # 36 splits: fused combine + projection
     torch.cuda.synchronize()
     _check(case, out_fused, heads=heads, tag="many_splits chunk=128 (36 splits)")
+
+
+def test_split_plan_of_the_benchmarked_shapes():
+    """The planner's split sizes for the benchmarked decode shapes on a
+    256-CU MI355X (chosen by measurement: one wave of workgroups, splits up
+    to 8192 tokens)."""
+    import mla_compressed_latent_amd as mla
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("split sizes are stated for 256 compute units")
+    cases = [  # (shape, batch, max_q_len, max_seq_len, expected tokens per split)
+        (SMALL_DSV2, 32, 1, 4096, 1024),
+        (SMALL_DSV2, 8, 1, 131072, 8192),
+        (SMALL_DSV2, 256, 2, 32770, 8192),
+        (SMALL_LLAMA, 64, 1, 8192, 2048),
+    ]
+    for shape, B, q, L, expect in cases:
+        case = GpuCase(workload("dsv2_b32_ctx4096", name="plan", shape=shape, batch=1, fixed_prefix=16))
+        got = mla.mla_decode_kv_chunk(case.layer, B, q, L)
+        assert got == expect, (shape.H, B, q, L, got)
