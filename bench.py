@@ -96,7 +96,7 @@ def parse():
     ap.add_argument("--path", choices=("auto", "absorbed", "expanded"), default="auto",
                     help="form of mla_extend for extend workloads")
     ap.add_argument("--form", choices=("auto", "unfolded", "folded"), default="auto",
-                    help="output projection form for project workloads")
+                    help="output projection form (project workloads) or query projection form (hidden)")
     return ap.parse_args()
 
 
@@ -184,7 +184,14 @@ def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
     for _ in range(R - 1):
         layers.append(mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv))
         caches.append(cache0.clone())
-    out_form = None
+    out_form = q_form = None
+    if wl.kind == "hidden":
+        q_form = {"auto": mla.mla_query_choose_form(cfg, int(wl.q_lens().sum())),
+                  "unfolded": mla.MLA_QUERY_UNFOLDED, "folded": mla.MLA_QUERY_FOLDED}[form]
+        w_q = up(wl.w_q())
+        for layer in layers:
+            mla.mla_fold_query(layer, w_q, w_uk, q_form)
+        del w_q
     if wl.kind == "project":
         out_form = {"auto": mla.mla_output_choose_form(cfg, int(wl.q_lens().sum())),
                     "unfolded": mla.MLA_OUTPUT_UNFOLDED, "folded": mla.MLA_OUTPUT_FOLDED}[form]
@@ -203,12 +210,17 @@ def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
         max_seq_len=int(seq_lens_np.max()), kv_chunk=kv_chunk,
         out=torch.empty((Tq, s.H, s.d_v), dtype=dt, device=dev),
         cache_bytes=cache_bytes, folded_bytes=folded_bytes, cfg=cfg, pool=pool, out_form=out_form,
+        q_form=q_form,
     )
     st["chunk"] = mla.mla_decode_kv_chunk(layer0, B, st["max_q_len"], st["max_seq_len"], kv_chunk)
     st["aws"] = torch.empty(max(1, mla.mla_append_workspace_bytes(layer0, Tq)), dtype=torch.uint8, device=dev)
     st["extend"] = wl.kind == "extend"
-    st["project"] = wl.kind == "project"
-    if st["project"]:
+    st["hidden"] = wl.kind == "hidden"
+    st["project"] = wl.kind in ("project", "hidden")   # both: graph replay of append + one call
+    if st["hidden"]:
+        st["dws"] = torch.empty(max(1, mla.mla_decode_hidden_workspace_bytes(
+            layer0, B, Tq, st["max_q_len"], st["max_seq_len"])), dtype=torch.uint8, device=dev)
+    elif st["project"]:
         st["y"] = torch.empty((Tq, s.d_model), dtype=dt, device=dev)
         st["dws"] = torch.empty(max(1, mla.mla_decode_project_workspace_bytes(
             layer0, B, Tq, st["max_q_len"], st["max_seq_len"])), dtype=torch.uint8, device=dev)
@@ -240,8 +252,12 @@ def run_step(st, i, ev=None, path=None):
                               workspace=st["aws"])
         if ev is not None:
             ev[1].record()
-        mla.mla_decode_project(layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["y"],
-                               st["max_q_len"], st["max_seq_len"], workspace=st["dws"])
+        if st["hidden"]:
+            mla.mla_decode_hidden(layer, st["x_new"], st["cu_q"], st["seq_lens"], st["table"], cache, st["out"],
+                                  st["max_q_len"], st["max_seq_len"], workspace=st["dws"])
+        else:
+            mla.mla_decode_project(layer, st["q"], st["cu_q"], st["seq_lens"], st["table"], cache, st["y"],
+                                   st["max_q_len"], st["max_seq_len"], workspace=st["dws"])
         if ev is not None:
             ev[2].record()
         return
@@ -572,29 +588,40 @@ def main_project(args, wl, st):
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / (reps * R)
-    folded = st["out_form"] == mla.MLA_OUTPUT_FOLDED
-    H, dc, dv, dm = s.H, s.d_c, s.d_v, s.d_model
-    w_bytes = 2 * H * dc * dm if folded else 2 * H * dv * (dc + dm)
+    H, dc, dv, dm, dn, dr = s.H, s.d_c, s.d_v, s.d_model, s.d_nope, s.d_rope
+    hidden = st["hidden"]
+    if hidden:
+        # query projection (with the absorb through W_uk when unfolded), then W_uv
+        folded = st["q_form"] == mla.MLA_QUERY_FOLDED
+        w_bytes = 2 * H * (dc + dr) * dm if folded else 2 * H * ((dn + dr) * dm + dn * dc)
+        other = 2 * H * dc * dv
+        call, form_key = "mla_decode_hidden", "query_form"
+    else:
+        folded = st["out_form"] == mla.MLA_OUTPUT_FOLDED
+        w_bytes = 2 * H * dc * dm if folded else 2 * H * dv * (dc + dm)
+        other = 2 * H * dc * dn
+        call, form_key = "mla_decode_project", "output_form"
     latent = int(st["seq_lens_np"].astype("int64").sum()) * s.cache_token_bytes
     call_s = phase[1] * 1e-3
-    achieved = (latent + w_bytes + 2 * H * dc * s.d_nope) / call_s / 1e9
+    achieved = (latent + w_bytes + other) / call_s / 1e9
     res = {
-        "metric": "MLA decode + output projection tokens/s, 1 GPU", "value": st["Tq"] / (ms_step * 1e-3),
+        "metric": ("MLA decode from the layer input tokens/s, 1 GPU" if hidden else
+                   "MLA decode + output projection tokens/s, 1 GPU"), "value": st["Tq"] / (ms_step * 1e-3),
         "unit": "tokens/s", "n_gpus": 1, "steps": reps * R, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic (seeded Gaussian hidden states and weights)",
         "config": {"workload": wl.name, "batch": wl.batch, "query_tokens": st["Tq"],
                    "max_context": st["max_seq_len"], "heads": H, "d_model": dm,
-                   "output_form": "folded" if folded else "unfolded", "rotated_copies": R},
-        "timing": "HIP graph replay of whole steps (append + mla_decode_project)",
-        "phase_ms": {"append": phase[0], "decode_project": phase[1]},
+                   form_key: "folded" if folded else "unfolded", "rotated_copies": R},
+        "timing": f"HIP graph replay of whole steps (append + {call})",
+        "phase_ms": {"append": phase[0], call[4:]: phase[1]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "mla_decode_project (all its kernels, HIP events around the call)",
-                     "algorithmic_bytes_per_launch": latent + w_bytes + 2 * H * dc * s.d_nope,
+                     "kernel": f"{call} (all its kernels, HIP events around the call)",
+                     "algorithmic_bytes_per_launch": latent + w_bytes + other,
                      "weights_streamed_bytes": w_bytes},
     }
-    log(f"{ms_step * 1e3:.1f} us/step (graph); decode+project {phase[1] * 1e3:.1f} us "
+    log(f"{ms_step * 1e3:.1f} us/step (graph); {call[4:]} {phase[1] * 1e3:.1f} us "
         f"({'folded' if folded else 'unfolded'}, weights {w_bytes / 1e6:.0f} MB)")
     print(json.dumps(res), flush=True)
 

@@ -138,6 +138,7 @@ class Workload:
     kind: str = "decode"              # "decode": the step is append + mla_decode;
                                       # "extend": append + mla_extend (long chunks);
                                       # "project": append + mla_decode_project
+                                      # "hidden": append + mla_decode_hidden
     layers: int = 0                   # > 0: a stack of this many layers sharing one
                                       # page-pool table (one timed pass = all layers)
 
@@ -297,6 +298,11 @@ WORKLOADS = {
         kind="project",
         description="bf16; DeepSeek-V2 shape, batch 32, every context 4096, q_len 1, decode and the "
                     "output projection W_o (the value up-projection folded into it or not)"),
+    "dsv2_b32_ctx4096_hidden": Workload(
+        "dsv2_b32_ctx4096_hidden", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
+        kind="hidden",
+        description="bf16; DeepSeek-V2 shape, batch 32, every context 4096, q_len 1, decode with the "
+                    "queries projected from the layer input (W_uk folded into W_q or not)"),
     "dsv2_60layers_b32_ctx4096": Workload(
         "dsv2_60layers_b32_ctx4096", DSV2, batch=32, seed=2, prefix_source="hidden", fixed_prefix=4095,
         layers=60,
