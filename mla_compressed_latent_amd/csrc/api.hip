@@ -806,8 +806,8 @@ mla_status mla_decode_hidden(const mla_layer* L, const void* x, const int32_t* c
                   MLA_PHASE_ALL, st);
   } else {
     // folded: the projection writes the attention's query rows directly
-    mla::launch_append_gemm_bf16(x, L->wq_p, part, total_q, hl.N, c.d_model, st);
-    mla::launch_query_finish(part, mla::append_ksplits_bf16(c.d_model), total_q, c.num_attention_heads,
+    const int ks = mla::launch_project_gemm(x, L->wq_p, part, total_q, hl.N, c.d_model, st);
+    mla::launch_query_finish(part, ks, total_q, c.num_attention_heads,
                              c.kv_lora_rank, c.qk_rope_head_dim, cu_q, seq_lens, batch, L->freq,
                              L->scale * 1.4426950408889634f, ws + d.off_abuf, st);
     decode_launch(L, x, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p,

@@ -126,8 +126,12 @@ void launch_fold_query(int form, const void* w_q, const void* w_uk, void* out, i
 void launch_query_finish(const float* part, int ks, int Tq, int H, int dc, int dr, const int32_t* cu_q,
                          const int32_t* seq_lens, int batch, const RopeFreq& freq, float qscale, void* abuf,
                          hipStream_t st);
+// part[s][M][N] (fp32) = the s-th split of a[M][K] . W^T for a tiled W (rows N,
+// contraction K, K a multiple of 256, N of 32); returns the number of splits
+// (at most K/256).
+int launch_project_gemm(const void* a, const void* w_tiled, float* part, int M, int N, int K, hipStream_t st);
 // y[M][N] (bf16) = a[M][K] . W^T for a tiled W (rows N, contraction K), via
-// split-K fp32 partials part[K/256][M][N] summed in split order.
+// launch_project_gemm's partials summed in split order.
 void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,
                     hipStream_t st);
 

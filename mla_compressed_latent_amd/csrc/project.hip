@@ -9,8 +9,8 @@
 //
 // Both are one plain matrix product of the query rows with a weight matrix
 // stored fragment-tiled at load (rows = the d_model outputs, contraction
-// index k), run by the split-K matrix-core GEMM of the append path and a
-// fixed-order reduction of its fp32 partials.
+// index k), run by a split-K matrix-core GEMM and a fixed-order reduction of
+// its fp32 partials.
 //
 // The queries themselves can come from the layer input the same way, with
 // the key up-projection kept apart or folded into the query projection
@@ -125,6 +125,43 @@ __global__ void fold_wuvo_kernel(const bf16* __restrict__ w_uv, const bf16* __re
   }
 }
 
+// part[ks][m][n] = sum over k in the ks-th run of KR consecutive 256-wide k
+// chunks of a[m][k] w[n][k]: one wave per (32 rows m, 32 outputs n, run),
+// the tiled weight as the A operand (contiguous fragments), a as the B
+// operand, one fp32 accumulator carried through the run -- the append GEMM's
+// block with KR times fewer split partials to write and sum, for the skinny
+// (few query rows) projections whose partials would otherwise rival the
+// weight bytes.
+template <int KR>
+__global__ __launch_bounds__(64) void project_gemm_kernel(const bf16* __restrict__ a, const bf16* __restrict__ w,
+                                                          float* __restrict__ part, int M, int N, int K) {
+  constexpr int NS = 16;   // fragments per 256-wide chunk
+  const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
+  const int t = blockIdx.x * 32 + l32, nb = blockIdx.y, ks = blockIdx.z;
+  const bf16* ar = a + (int64_t)min(t, M - 1) * K + 8 * g;
+  f32x16 acc = zero_f32x16();
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    const int kc = ks * KR + r;
+    bf16x8 wa[NS], xb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      wa[s] = load_fragment(w, nb, kc * NS + s, K, lane);
+      xb[s] = load_bf16x8(ar + kc * 256 + 16 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32(wa[s], xb[s], acc);
+  }
+  if (t < M) {
+    float* out = part + ((int64_t)ks * M + t) * N + nb * 32 + 4 * g;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+      *reinterpret_cast<f32x4*>(out + 8 * r4) = v;
+    }
+  }
+}
+
 // y[m][n] = sum over splits s (in order) of part[s][m][n], rounded to bf16.
 __global__ void sum_splits_kernel(const float* __restrict__ part, int ks, int M, int N,
                                   bf16* __restrict__ y) {
@@ -163,12 +200,31 @@ void launch_query_finish(const float* part, int ks, int Tq, int H, int dc, int d
                                                                    batch, freq, qscale, (bf16*)abuf);
 }
 
+int launch_project_gemm(const void* a, const void* w_tiled, float* part, int M, int N, int K, hipStream_t st) {
+  // the longest run of k chunks that still leaves about eight waves per
+  // compute unit
+  const int chunks = K / 256, mb = (M + 31) / 32, nb = N / 32;
+  int kr = 1;
+  for (int c = 8; c > 1; c /= 2)
+    if (chunks % c == 0 && (int64_t)mb * nb * (chunks / c) >= 2048) {
+      kr = c;
+      break;
+    }
+  const dim3 grid(mb, nb, chunks / kr);
+  switch (kr) {
+    case 8: project_gemm_kernel<8><<<grid, 64, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+    case 4: project_gemm_kernel<4><<<grid, 64, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+    case 2: project_gemm_kernel<2><<<grid, 64, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+    default: project_gemm_kernel<1><<<grid, 64, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K);
+  }
+  return chunks / kr;
+}
+
 void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,
                     hipStream_t st) {
-  launch_append_gemm_bf16(a, w_tiled, part, M, N, K, st);
+  const int ks = launch_project_gemm(a, w_tiled, part, M, N, K, st);
   const int64_t n = (int64_t)M * N;
-  sum_splits_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, append_ksplits_bf16(K), M, N,
-                                                                 (bf16*)y);
+  sum_splits_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, ks, M, N, (bf16*)y);
 }
 
 }  // namespace mla

@@ -61,6 +61,15 @@ def test_project_dsv2_heads(form):
     _run(wl, form)
 
 
+def test_project_dsv2_wide_output():
+    """d_model 4096, unfolded: the projection GEMM carries its accumulator
+    through runs of 4 256-wide k chunks per split."""
+    shape = dataclasses.replace(DSV2, d_model=4096)
+    wl = workload("dsv2_ragged_paged_256", name="project_dsv2_wide", shape=shape, batch=2, max_prefix=300,
+                  prefix_source="hidden", seed=54)
+    _run(wl, UNF)
+
+
 def test_project_errors():
     wl = workload("dsv2_ragged_paged_256", name="project_err", shape=dataclasses.replace(
         DSV2, d_model=256, num_attention_heads=4, qk_nope_head_dim=64, v_head_dim=64), batch=2,

@@ -66,6 +66,15 @@ def test_query_dsv2_heads(form):
     _run(wl, form)
 
 
+@pytest.mark.parametrize("form", [UNF, FOL])
+def test_query_dsv2_wide_input(form):
+    """d_model 2048: the projection GEMM carries its accumulator through runs
+    of 2 (unfolded) and 8 (folded) 256-wide k chunks per split."""
+    wl = workload("dsv2_ragged_paged_256", name="query_dsv2_wide", shape=dataclasses.replace(DSV2, d_model=2048),
+                  batch=2, max_prefix=300, prefix_source="hidden", seed=65)
+    _run(wl, form)
+
+
 def test_query_forms_agree_and_auto_folds_narrow_model():
     """d_nope 192 at d_model 256: the chooser folds; both forms agree with the
     oracle and with each other."""
