@@ -162,6 +162,73 @@ __global__ __launch_bounds__(64) void project_gemm_kernel(const bf16* __restrict
   }
 }
 
+// The same product with the activation chunk shared through LDS: four waves
+// per workgroup take four consecutive 32-output blocks; per 256-wide k chunk
+// the workgroup copies the 32 x 256 activation tile once (coalesced 16-byte
+// pieces; rows padded by 16 bytes so the 32 rows of an operand read start 4
+// banks apart) and each wave reads its B operands from there, instead of
+// every wave fetching the tile through its own 32-row strided loads.  The
+// next chunk's weight fragments and activation pieces are loaded while the
+// current chunk's products run.  N must be a multiple of 128.
+constexpr int kXRow = 256 + 8;   // padded LDS row (elements)
+
+template <int KR>
+__global__ __launch_bounds__(256) void project_gemm_lds_kernel(const bf16* __restrict__ a,
+                                                               const bf16* __restrict__ w,
+                                                               float* __restrict__ part, int M, int N,
+                                                               int K) {
+  constexpr int NS = 16;
+  __shared__ __attribute__((aligned(16))) bf16 xs[32 * kXRow];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.x * 32, nb = blockIdx.y * 4 + wave, ks = blockIdx.z;
+  // activation pieces of this thread: rows (tid + 256 j) / 32, 16-byte column (tid % 32)
+  const int prow = tid >> 5, pcol = (tid & 31) * 8;
+  auto load_x = [&](int kc, bf16x8 (&dst)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = load_bf16x8(a + (int64_t)min(m0 + prow + 8 * j, M - 1) * K + kc * 256 + pcol);
+  };
+  auto load_w = [&](int kc, bf16x8 (&dst)[NS]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) dst[s] = load_fragment(w, nb, kc * NS + s, K, lane);
+  };
+  bf16x8 xg[4], wa[NS];
+  load_x(ks * KR, xg);
+  load_w(ks * KR, wa);
+  f32x16 acc = zero_f32x16();
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x8*>(&xs[(prow + 8 * j) * kXRow + pcol]) = xg[j];
+    __syncthreads();
+    bf16x8 wn[NS];
+    if (r + 1 < KR) {
+      load_x(ks * KR + r + 1, xg);
+      load_w(ks * KR + r + 1, wn);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&xs[l32 * kXRow + 16 * s + 8 * g]);
+      acc = mfma32(wa[s], xb, acc);
+    }
+    if (r + 1 < KR) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) wa[s] = wn[s];
+      __syncthreads();
+    }
+  }
+  const int t = m0 + l32;
+  if (t < M) {
+    float* out = part + ((int64_t)ks * M + t) * N + nb * 32 + 4 * g;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+      *reinterpret_cast<f32x4*>(out + 8 * r4) = v;
+    }
+  }
+}
+
 // y[m][n] = sum over splits s (in order) of part[s][m][n], rounded to bf16.
 __global__ void sum_splits_kernel(const float* __restrict__ part, int ks, int M, int N,
                                   bf16* __restrict__ y) {
@@ -210,6 +277,16 @@ int launch_project_gemm(const void* a, const void* w_tiled, float* part, int M, 
       kr = c;
       break;
     }
+  if (nb % 4 == 0) {
+    const dim3 grid(mb, nb / 4, chunks / kr);
+    switch (kr) {
+      case 8: project_gemm_lds_kernel<8><<<grid, 256, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+      case 4: project_gemm_lds_kernel<4><<<grid, 256, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+      case 2: project_gemm_lds_kernel<2><<<grid, 256, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
+      default: project_gemm_lds_kernel<1><<<grid, 256, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K);
+    }
+    return chunks / kr;
+  }
   const dim3 grid(mb, nb, chunks / kr);
   switch (kr) {
     case 8: project_gemm_kernel<8><<<grid, 64, 0, st>>>((const bf16*)a, (const bf16*)w_tiled, part, M, N, K); break;
