@@ -87,6 +87,58 @@ def test_query_forms_agree_and_auto_folds_narrow_model():
     assert d <= 1e-2, d
 
 
+@pytest.mark.parametrize("form", [UNF, FOL])
+def test_query_fp8_cache(form):
+    """Queries from the layer input over FP8 pages (the oracle dequantizes
+    with its own row quantizer)."""
+    wl = workload("dsv2_ragged_paged_256", name="query_fp8",
+                  shape=dataclasses.replace(DSV2, d_model=512, cache_format="fp8"), batch=3, max_prefix=400,
+                  prefix_source="hidden", paging="random", spare_page_frac=0.2, seed=66)
+    _run(wl, form)
+
+
+@pytest.mark.parametrize("form", [UNF, FOL])
+def test_query_graph_replay_matches_eager(form):
+    """mla_decode_hidden captured as a graph: three replays, with eager calls
+    between them, each bit-identical to the eager call."""
+    wl = workload("dsv2_ragged_paged_256", name="query_graph", shape=dataclasses.replace(DSV2, d_model=512),
+                  batch=3, max_prefix=300, prefix_source="hidden", seed=67)
+    print(f"[query] graph case form {form}", flush=True)
+    s = wl.shape
+    case = GpuCase(wl)
+    case.append_new()
+    mla.mla_fold_query(case.layer, to_dev(wl.w_q(), torch.bfloat16), to_dev(case.w_uk, torch.bfloat16), form)
+    Tq = case.q.shape[0]
+    ws = torch.empty(mla.mla_decode_hidden_workspace_bytes(case.layer, wl.batch, Tq, case.max_q_len,
+                                                           case.max_seq_len), dtype=torch.uint8, device="cuda")
+
+    def call(out):
+        mla.mla_decode_hidden(case.layer, case.x_new_dev, case.cu_q, case.seq_lens, case.page_table, case.cache,
+                              out, case.max_q_len, case.max_seq_len, workspace=ws)
+
+    eager = torch.empty((Tq, s.H, s.d_v), dtype=torch.bfloat16, device="cuda")
+    call(eager)
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            call(out_g)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    other = torch.empty_like(eager)
+    for rep in range(3):
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), f"graph replay {rep} differs from the eager result"
+        call(other)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+
+
 def test_query_errors():
     wl = workload("dsv2_ragged_paged_256", name="query_err", shape=SMALL, batch=2, max_prefix=50,
                   prefix_source="hidden", seed=64)
