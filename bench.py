@@ -275,7 +275,7 @@ def run_step(st, i, ev=None, path=None):
             ev[2].record()
         return
     if ev is None and not st["separate"]:
-        # the whole step in one call: the append GEMM and the query absorb share a launch
+        # the whole step in one call: the query absorb shares a launch with the append finish
         mla.mla_decode_step(layer, st["x_new"], st["cu_q"], st["prefix"], st["q"], st["cu_q"], st["seq_lens"],
                             st["table"], cache, st["out"], st["max_q_len"], st["max_seq_len"], st["kv_chunk"],
                             workspace=st["sws"])
@@ -509,7 +509,7 @@ def main():
         "latent_cache_frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,
         "timing": ("HIP graph replay of whole steps ("
                    + ("mla_append_latent + mla_decode" if st["separate"] else
-                      "mla_decode_step: append + decode, the append GEMM and the query absorb in one launch")
+                      "mla_decode_step: append + decode, the query absorb and the append finish in one launch")
                    + "); one graph holds one step on each of the R rotated layer copies; phase_us and "
                    "eager_ms_per_step time the separate calls"),
         "ms_per_step_p10_p50_p90": [pct(per_step, 0.1), pct(per_step, 0.5), pct(per_step, 0.9)],

@@ -225,11 +225,13 @@ mla_status mla_decode_phases(const mla_layer* layer, const void* q, const int32_
  * rows (x, cu_new, prefix_lens, total_new as there) followed by mla_decode
  * of the queries (q, cu_q, seq_lens, ... as there; seq_lens count the rows
  * just appended), with the same results bit for bit, in fewer launches: on
- * bf16 layers the append GEMM and the query absorb, independent of each
- * other, share one launch ("Multi-head Latent Attention: the KV cache,
- * compressed": section "Store the archive, not the files" for the latent
- * x W_dkv that a step caches, section "Absorption: the part that makes it
- * free" for folding W_uk onto the query; neither product needs the other).
+ * bf16 layers the query absorb shares a launch with the append's finish (bf16
+ * pages: the GEMM runs first, then the finish beside the absorb) or with the
+ * append GEMM (FP8 pages) -- work independent of each other ("Multi-head
+ * Latent Attention: the KV cache, compressed": section "Store the archive,
+ * not the files" for the latent x W_dkv that a step caches, section
+ * "Absorption: the part that makes it free" for folding W_uk onto the query;
+ * neither needs the other).
  *   workspace  device, 256-byte aligned, >= mla_decode_step_workspace_bytes
  *              (the decode workspace, then the append's)
  * Errors: those of mla_append_latent and mla_decode; nothing is enqueued

@@ -491,8 +491,18 @@ mla_status mla_decode_step(const mla_layer* L, const void* x, const int32_t* cu_
   float* part = (float*)(ws + off_app);
   const int D = c.kv_lora_rank + c.qk_rope_head_dim;
   uint32_t phases = MLA_PHASE_ALL;
-  if (total_new > 0) {
+  if (total_new > 0 && L->elem == 2 && c.cache_format == MLA_CACHE_DTYPE) {
+    // the append GEMM, then the query absorb with the append finish
+    mla::launch_append_gemm_bf16(x, L->wdkv_t, part, total_new, D, c.d_model, st);
+    mla::launch_absorb_finish(q, L->wuk_p, ws + d.off_abuf, cu_q, seq_lens, batch, total_q, max_q_len,
+                              c.num_attention_heads, c.qk_nope_head_dim, c.qk_rope_head_dim, c.kv_lora_rank,
+                              L->freq, L->scale * 1.4426950408889634f, part,
+                              mla::append_ksplits_bf16(c.d_model), total_new, cu_new, prefix_lens, page_table,
+                              max_pages, cache, c.page_size, st);
+    phases = MLA_PHASE_ATTEND | MLA_PHASE_OUTPUT;
+  } else if (total_new > 0) {
     if (L->elem == 2) {
+      // FP8 pages: the append GEMM with the query absorb, then the quantizing finish
       mla::launch_absorb_append(q, L->wuk_p, ws + d.off_abuf, cu_q, seq_lens, batch, total_q, max_q_len,
                                 c.num_attention_heads, c.qk_nope_head_dim, c.qk_rope_head_dim,
                                 c.kv_lora_rank, L->freq, L->scale * 1.4426950408889634f, x, L->wdkv_t, part,

@@ -166,6 +166,30 @@ __global__ __launch_bounds__(64) void absorb_append_bf16_kernel(
                        bid - app_blocks);
 }
 
+// The query absorb with its rope rotation and the append finish in one
+// launch (the append GEMM ran in the launch before): finish blocks first
+// (new token bid / fin_py, pair block bid % fin_py, for bid < fin_blocks),
+// then the absorb blocks.  The finish reads only the GEMM's partials and
+// writes only the new rows; the absorb reads only the queries and W_uk: the
+// short finish runs under the longer absorb.
+template <int NS, int JB>
+__global__ __launch_bounds__(64) void absorb_finish_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ wuk, bf16* __restrict__ abuf,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int Tq, int H, int dr,
+    int dc, int gemm_blocks, int TC, const RopeFreq freq, float qscale, const float* __restrict__ part,
+    int ksplits, int T_new, const int32_t* __restrict__ cu_new, const int32_t* __restrict__ prefix_lens,
+    const int32_t* __restrict__ page_table, int max_pages, int batch, bf16* __restrict__ cache,
+    int page_size, int fin_py, int fin_blocks) {
+  const int bid = blockIdx.x;
+  if (bid < fin_blocks) {
+    append_finish_block<bf16>(part, ksplits, T_new, cu_new, prefix_lens, page_table, max_pages, batch, cache,
+                              page_size, dc, dr, 0.f, freq, bid / fin_py, bid % fin_py);
+    return;
+  }
+  absorb_block<NS, JB>(q, wuk, abuf, cu_q, seq_lens, Tq, H, dr, dc, gemm_blocks, TC, freq, qscale,
+                       bid - fin_blocks);
+}
+
 // out^T block = W_uv_h^T (32 value rows x d_c) . o_lat^T (d_c x 32 tokens).
 // One wave per (32-token block, head, 32 value columns); the 32 k-steps of
 // both operands stream in groups of 8, two groups in flight.
@@ -491,6 +515,32 @@ void launch_absorb_append(const void* q, const void* wuk, void* abuf, const int3
     MLA_FUSED_CASE(2, 4) MLA_FUSED_CASE(4, 4) MLA_FUSED_CASE(6, 4) MLA_FUSED_CASE(8, 4)
     MLA_FUSED_CASE(10, 2) MLA_FUSED_CASE(12, 2) MLA_FUSED_CASE(14, 2) MLA_FUSED_CASE(16, 2)
 #undef MLA_FUSED_CASE
+    default: break;   // excluded by the config check
+  }
+}
+
+void launch_absorb_finish(const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                          const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn,
+                          int dr, int dc, const RopeFreq& freq, float qscale, const float* part,
+                          int ksplits, int T_new, const int32_t* cu_new, const int32_t* prefix_lens,
+                          const int32_t* page_table, int max_pages, void* cache, int page_size,
+                          hipStream_t st) {
+  const AbsorbGrid a = absorb_grid(batch, Tq, max_q_len, H, dn, dc);
+  const int gemm_blocks = a.gemm_blocks, TC = a.TC;
+  const int fin_py = ((dc + dr) / 2 + 63) / 64;
+  const int fin_blocks = T_new * fin_py;
+  const unsigned blocks = (unsigned)(fin_blocks + a.blocks);
+  switch (dn / 16 * 8 + a.jb) {
+#define MLA_FIN_CASE(NS, JB)                                                                        \
+  case NS * 8 + JB:                                                                                 \
+    absorb_finish_bf16_kernel<NS, JB><<<blocks, 64, 0, st>>>(                                       \
+        (const bf16*)q, (const bf16*)wuk, (bf16*)abuf, cu_q, seq_lens, Tq, H, dr, dc, gemm_blocks,  \
+        TC, freq, qscale, part, ksplits, T_new, cu_new, prefix_lens, page_table, max_pages, batch,  \
+        (bf16*)cache, page_size, fin_py, fin_blocks);                                               \
+    break;
+    MLA_FIN_CASE(2, 4) MLA_FIN_CASE(4, 4) MLA_FIN_CASE(6, 4) MLA_FIN_CASE(8, 4)
+    MLA_FIN_CASE(10, 2) MLA_FIN_CASE(12, 2) MLA_FIN_CASE(14, 2) MLA_FIN_CASE(16, 2)
+#undef MLA_FIN_CASE
     default: break;   // excluded by the config check
   }
 }

@@ -54,6 +54,15 @@ void launch_absorb_append(const void* q, const void* wuk, void* abuf, const int3
                           const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn,
                           int dr, int dc, const RopeFreq& freq, float qscale, const void* x,
                           const void* wdkv, float* part, int M, int N, int K, hipStream_t st);
+// bf16 layers with bf16 pages: launch_absorb's work and the append finish of
+// launch_append_gemm_bf16's partials (part, ksplits, T_new new tokens) as one
+// launch of one-wave blocks.
+void launch_absorb_finish(const void* q, const void* wuk, void* abuf, const int32_t* cu_q,
+                          const int32_t* seq_lens, int batch, int Tq, int max_q_len, int H, int dn,
+                          int dr, int dc, const RopeFreq& freq, float qscale, const float* part,
+                          int ksplits, int T_new, const int32_t* cu_new, const int32_t* prefix_lens,
+                          const int32_t* page_table, int max_pages, void* cache, int page_size,
+                          hipStream_t st);
 // out[t][h][v] = sum_j olat[t][h][j] * wuv_p[h][v][j]
 void launch_out_proj(int elem, const void* olat, const void* wuv_p, void* out, int Tq, int H, int dc,
                      int dv, hipStream_t st);

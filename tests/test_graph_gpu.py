@@ -117,7 +117,7 @@ def test_two_stream_graph_matches_eager():
 
 
 def test_decode_step_graph_replay_matches_eager():
-    """mla_decode_step (the append GEMM and the query absorb in one launch)
+    """mla_decode_step (the query absorb and the append finish in one launch)
     captured as a graph: three replays, with eager steps between them, each
     bit-identical to the eager call."""
     wl = workload("dsv2_ragged_paged_256", name="graph_step", batch=4, max_prefix=250)

@@ -1,6 +1,7 @@
 """GPU: mla_decode_step, one layer's whole decode step (append the new tokens'
-rows, then attend with the queries) with the append GEMM and the query absorb
-in one launch, against mla_append_latent followed by mla_decode on the same
+rows, then attend with the queries) with the query absorb sharing a launch
+with the append finish (bf16 pages) or the append GEMM (FP8 pages), against
+mla_append_latent followed by mla_decode on the same
 inputs: the outputs and every byte of the cache agree bit for bit (the same
 device arithmetic runs in a different grouping of launches).  One case is
 also checked against the float64 oracle to the decode parity tolerances.
