@@ -75,6 +75,16 @@ def test_query_dsv2_wide_input(form):
     _run(wl, form)
 
 
+@pytest.mark.parametrize("form", [UNF, FOL])
+def test_query_two_heads_d_nope_96(form):
+    """Two heads of d_nope 96: the unfolded projection has 320 outputs (not a
+    multiple of 128), so it runs the one-wave GEMM blocks instead of the
+    four-wave LDS-shared ones."""
+    wl = workload("dsv2_ragged_paged_256", name="query_h2", shape=Shape(256, 2, 96, 64, 64, 512), batch=3,
+                  max_prefix=300, prefix_source="hidden", seed=68)
+    _run(wl, form)
+
+
 def test_query_forms_agree_and_auto_folds_narrow_model():
     """d_nope 192 at d_model 256: the chooser folds; both forms agree with the
     oracle and with each other."""
