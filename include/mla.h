@@ -411,6 +411,9 @@ size_t mla_output_folded_bytes(const mla_config* cfg, int32_t form);
 mla_status mla_fold_output(mla_layer* layer, const void* w_uv, const void* w_o, int32_t form,
                            void* folded, size_t folded_bytes, void* hip_stream);
 
+/* Workspace bytes of mla_decode_project for these host bounds, by the form
+ * the layer was folded with (0 when no output projection is folded or the
+ * sizes are invalid). */
 size_t mla_decode_project_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
                                           int32_t max_q_len, int32_t max_seq_len);
 
@@ -468,6 +471,9 @@ size_t mla_query_folded_bytes(const mla_config* cfg, int32_t form);
 mla_status mla_fold_query(mla_layer* layer, const void* w_q, const void* w_uk, int32_t form,
                           void* folded, size_t folded_bytes, void* hip_stream);
 
+/* Workspace bytes of mla_decode_hidden for these host bounds, by the form the
+ * layer was folded with (0 when no query projection is folded or the sizes
+ * are invalid). */
 size_t mla_decode_hidden_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
                                          int32_t max_q_len, int32_t max_seq_len);
 
