@@ -230,14 +230,25 @@ __global__ __launch_bounds__(256) void project_gemm_lds_kernel(const bf16* __res
 }
 
 // y[m][n] = sum over splits s (in order) of part[s][m][n], rounded to bf16.
+// Four consecutive outputs per thread (N is a multiple of 32): 16-byte loads
+// of every split, eight in flight.
 __global__ void sum_splits_kernel(const float* __restrict__ part, int ks, int M, int N,
                                   bf16* __restrict__ y) {
   const int64_t n = (int64_t)M * N;
-  const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t o = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (o >= n) return;
-  float acc = 0.f;
-  for (int s = 0; s < ks; ++s) acc += part[(int64_t)s * n + o];
-  y[o] = from_f32<bf16>(acc);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < ks; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + s * n + o);
+    a0 += v[0];
+    a1 += v[1];
+    a2 += v[2];
+    a3 += v[3];
+  }
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 r = {from_f32<bf16>(a0), from_f32<bf16>(a1), from_f32<bf16>(a2), from_f32<bf16>(a3)};
+  *reinterpret_cast<bf16x4*>(y + o) = r;
 }
 
 }  // namespace
@@ -300,8 +311,8 @@ int launch_project_gemm(const void* a, const void* w_tiled, float* part, int M, 
 void launch_project(const void* a, const void* w_tiled, float* part, void* y, int M, int N, int K,
                     hipStream_t st) {
   const int ks = launch_project_gemm(a, w_tiled, part, M, N, K, st);
-  const int64_t n = (int64_t)M * N;
-  sum_splits_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, ks, M, N, (bf16*)y);
+  const int64_t n4 = (int64_t)M * N / 4;
+  sum_splits_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(part, ks, M, N, (bf16*)y);
 }
 
 }  // namespace mla
