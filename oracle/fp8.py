@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/mla_oracle.py``).
 Source: "Multi-head Latent Attention and KV Cache Compression" (jongkwan.dev),
 section "Moving a trained MHA model over": the cached latent can be quantized
 further, with scale correction; the pages name no format, so the reading
-taken here (listed in the design doc) is the OCP 8-bit float E4M3: 1 sign bit, 4
+taken here is the OCP 8-bit float E4M3: 1 sign bit, 4
 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
 subnormals m * 2^-9; no infinities; only S.1111.111 is NaN, so the largest
 finite magnitude is 1.75 * 2^8 = 448.  One power-of-two scale per row:

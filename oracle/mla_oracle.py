@@ -28,7 +28,7 @@ Sources (web pages, cited by title and section):
 * "Multi-Head Latent Attention (MLA)" (superteams.ai glossary), section "The
   Mechanism": cached element count per token is kv_lora_rank + rope dim.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Rotary embedding pairs interleaved elements (2i, 2i+1) and rotates each
   pair counter-clockwise by ``p * base**(-2i/d_rope)``; positions are
