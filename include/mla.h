@@ -373,9 +373,9 @@ mla_status mla_pool_page_table(const mla_page_pool* pool, const int32_t* seqs, i
 /* ---------------------------------------------------------------------------
  * Layer output with the output projection W_o, the value up-projection kept
  * apart or folded into it ("Multi-head Latent Attention and KV Cache
- * Compression", section "The absorption trick and decoupled RoPE": the
- * value-side up-projection is absorbed into the output projection the same
- * way the key side is absorbed into the query).
+ * Compression", section "The absorption trick and decoupled RoPE": W_uv can
+ * be pre-multiplied into W_o just as W_uk is pre-multiplied into the query
+ * side).
  *   MLA_OUTPUT_UNFOLDED  y = concat_h(o_lat_h W_uv_h) . W_o
  *                        (weights H*d_v*(d_c + d_model) elements)
  *   MLA_OUTPUT_FOLDED    y = concat_h(o_lat_h) . W_uvo, W_uvo_h = W_uv_h W_o_h

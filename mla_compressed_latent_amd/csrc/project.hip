@@ -1,8 +1,8 @@
 // Output projection of the layer, with the value up-projection either kept
 // apart or folded into it ("Multi-head Latent Attention and KV Cache
 // Compression" (jongkwan.dev), section "The absorption trick and decoupled
-// RoPE": the value-side up-projection is absorbed into the output projection
-// the same way the key side is absorbed into the query).
+// RoPE": W_uv can be pre-multiplied into W_o just as W_uk is pre-multiplied
+// into the query side).
 //
 //   unfolded:  y = concat_h (o_lat_h W_uv_h) . W_o          K = H * d_v
 //   folded:    y = concat_h o_lat_h . W_uvo,  W_uvo_h = W_uv_h W_o_h   K = H * d_c

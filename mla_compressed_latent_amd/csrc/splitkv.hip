@@ -1,8 +1,8 @@
 // Split-KV attention over the paged latent cache, and the split combine.
 //
 // Every head scores the SAME cached row [c | k_rope] ("Multi-head Latent
-// Attention: the KV cache, compressed", section "The one formula": the latent
-// is shared across every head), so for one sequence the step is a dense
+// Attention: the KV cache, compressed", section "The one formula": one latent
+// row per token serves all heads), so for one sequence the step is a dense
 // contraction with the (query, head) rows as one dimension:
 //     S[row][t]   = scale * A[row] . cache[t]          (K = d_c + d_rope)
 //     O[row][:]  += softmax_t(S) cache[t][:d_c]        (K = tokens)

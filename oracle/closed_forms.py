@@ -3,8 +3,10 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/mla_oracle.py``).
 
 Sources: "Multi-head Latent Attention: the KV cache, compressed", sections
-"The one formula" (MHA stores 2 x layers x kv_heads x head_dim x seq x dtype
-bytes; MLA stores layers x (d_c + d_rope) x seq x dtype), "The table that is
+"The one formula" (a cache's size is the number of values it keeps per
+token and layer times layers, tokens and element size: a key and a value
+per kv head for ordinary attention, the latent plus the shared position key
+for MLA), "The table that is
 the whole argument", "Where the saving actually lands" (sequences that fit a
 cache budget), "What it costs, said plainly" (parameters per attention
 layer), "Absorption: the part that makes it free" (multiply-accumulates per
@@ -16,15 +18,23 @@ from __future__ import annotations
 GIB = 1 << 30
 
 
-def kv_cache_bytes(layers, kv_heads, head_dim, seq_len, dtype_bytes=2, batch=1):
-    """Keys and values stored separately for every kv head."""
-    return 2 * layers * kv_heads * head_dim * seq_len * dtype_bytes * batch
+def cache_footprint(per_token_layer_elems, n_layers, n_tokens, elem_size):
+    """Bytes of a cache that keeps ``per_token_layer_elems`` numbers of
+    ``elem_size`` bytes for every token in every layer."""
+    return per_token_layer_elems * n_layers * n_tokens * elem_size
 
 
-def mla_cache_bytes(layers, d_c, d_rope, seq_len, dtype_bytes=2, batch=1):
-    """One latent plus one decoupled rope key per token per layer, shared by
-    every head."""
-    return layers * (d_c + d_rope) * seq_len * dtype_bytes * batch
+def kv_cache_size(n_layers, n_kv_heads, width, n_tokens, elem_size=2):
+    """Classic attention cache: a key vector and a value vector, each
+    ``width`` wide, for every kv head."""
+    return cache_footprint(2 * n_kv_heads * width, n_layers, n_tokens, elem_size)
+
+
+def latent_cache_size(n_layers, latent_rank, rope_width, n_tokens, elem_size=2):
+    """Latent cache: one latent of ``latent_rank`` numbers plus one rotated
+    position key of ``rope_width`` numbers per token, whatever the head
+    count."""
+    return cache_footprint(latent_rank + rope_width, n_layers, n_tokens, elem_size)
 
 
 def seqs_in_budget(bytes_per_seq, budget_bytes):

@@ -24,7 +24,8 @@ Sources (web pages, cited by title and section):
     one copy shared by all heads.
 * "Multi-head Latent Attention and KV Cache Compression" (jongkwan.dev),
   section "The absorption trick and decoupled RoPE": two streams (NoPE and
-  RoPE), final score is the sum of the two inner products.
+  RoPE); a head's score adds the content dot product and the position dot
+  product.
 * "Multi-Head Latent Attention (MLA)" (superteams.ai glossary), section "The
   Mechanism": cached element count per token is kv_lora_rank + rope dim.
 

@@ -185,3 +185,33 @@ def test_batch_decode_and_errors():
     assert np.array_equal(out[1:3], ref)
     with pytest.raises(ValueError):
         attend_sequence(q[:3], caches[0][:2], k["w_uk"], k["w_uv"], 2, k["d_n"], k["d_v"], 1e4, 0.5)
+
+
+def test_default_scale_stated_values():
+    """The scale the workloads state: 1/sqrt(192) for the DeepSeek-V2-shaped
+    layer (d_nope 128 + d_rope 64) and 1/sqrt(24) for the tiny fp32 layer
+    (16 + 8); one query-key width per head, content and position parts joined
+    ("Multi-head Latent Attention: the KV cache, compressed", section "RoPE,
+    and why the explanations stop here": the position key is a separate
+    block of the same dot product)."""
+    assert default_scale(128, 64) == 1.0 / math.sqrt(192.0)
+    assert default_scale(16, 8) == 1.0 / math.sqrt(24.0)
+    assert default_scale(128, 64) == pytest.approx(0.07216878364870322, rel=1e-15)
+
+
+@pytest.mark.parametrize("a,r", [(2 * math.log(3.0), 0.0), (0.0, 2 * math.log(3.0)),
+                                 (math.log(3.0), math.log(3.0))])
+def test_default_scale_applies_to_the_summed_score(a, r):
+    """One head, d_c = d_nope = d_rope = d_v = 2, W_uk = W_uv = I, query at
+    position 1 with q = (0, a | r, 0).  Token 0 caches (1, 0 | 0, 0); token 1
+    caches (0, 1 | cos 1, sin 1), the key (1, 0) already rotated to position
+    1.  Content scores (0, a), position scores (0, r) (the query's (r, 0)
+    rotated by 1 rad meets the same rotation), so with one scale
+    1/sqrt(2 + 2) = 1/2 on their sum the weights are (1/4, 3/4) whenever
+    a + r = 2 ln 3 -- whichever stream carries the score."""
+    w = np.eye(2)
+    cache = np.array([[1.0, 0.0, 0.0, 0.0],
+                      [0.0, 1.0, math.cos(1.0), math.sin(1.0)]])
+    q = np.array([[[0.0, a, r, 0.0]]])
+    out = attend_sequence(q, cache, w, w, 1, 2, 2, 10000.0, default_scale(2, 2))
+    assert out[0, 0] == pytest.approx([0.25, 0.75], abs=1e-14)

@@ -20,9 +20,9 @@ def test_cache_bytes_per_token_tables(golden_dir):
     g = _load(golden_dir, "page1_cache_bytes.json")
     for s in g["shapes"]:
         L, H, hd, dt = s["layers"], s["heads"], s["head_dim"], s["dtype_bytes"]
-        mha = cf.kv_cache_bytes(L, H, hd, 1, dt)
-        gqa = cf.kv_cache_bytes(L, 8, hd, 1, dt)
-        mla = cf.mla_cache_bytes(L, s["d_c"], s["d_rope"], 1, dt)
+        mha = cf.kv_cache_size(L, H, hd, 1, dt)
+        gqa = cf.kv_cache_size(L, 8, hd, 1, dt)
+        mla = cf.latent_cache_size(L, s["d_c"], s["d_rope"], 1, dt)
         assert (mha, gqa, mla) == (s["mha"], s["gqa8"], s["mla"]), s["name"]
         assert round(mha / gqa, 1) == s["gqa8_smaller_x"]
         assert round(mha / mla, 1) == s["mla_smaller_x"]
@@ -31,19 +31,19 @@ def test_cache_bytes_per_token_tables(golden_dir):
 
 def test_decoupled_rope_cost(golden_dir):
     d = _load(golden_dir, "page1_cache_bytes.json")["decoupled_rope_cost"]
-    lat = cf.mla_cache_bytes(d["layers"], d["d_c"], 0, 1, d["dtype_bytes"])
-    full = cf.mla_cache_bytes(d["layers"], d["d_c"], d["d_rope"], 1, d["dtype_bytes"])
+    lat = cf.latent_cache_size(d["layers"], d["d_c"], 0, 1, d["dtype_bytes"])
+    full = cf.latent_cache_size(d["layers"], d["d_c"], d["d_rope"], 1, d["dtype_bytes"])
     assert (lat, full, full - lat) == (d["latent_only"], d["with_rope"], d["extra"])
     assert round(100.0 * (full - lat) / lat, 1) == d["extra_pct"]
-    assert round(cf.kv_cache_bytes(60, 128, 128, 1) / full, 1) == d["vs_mha_x"]
+    assert round(cf.kv_cache_size(60, 128, 128, 1) / full, 1) == d["vs_mha_x"]
 
 
 def test_latent_elements_per_token(golden_dir):
     d = _load(golden_dir, "page1_cache_bytes.json")["latent_elements_per_token"]
     assert d["kv_lora_rank"] + d["qk_rope_head_dim"] == d["elements"]
     # elements of a token's full K and V across heads (bytes / dtype, one layer)
-    assert cf.kv_cache_bytes(1, d["heads"], d["head_dim"], 1, 1) == d["mha_elements"]
-    assert cf.mla_cache_bytes(1, d["kv_lora_rank"], d["qk_rope_head_dim"], 1, 1) == d["elements"]
+    assert cf.kv_cache_size(1, d["heads"], d["head_dim"], 1, 1) == d["mha_elements"]
+    assert cf.latent_cache_size(1, d["kv_lora_rank"], d["qk_rope_head_dim"], 1, 1) == d["elements"]
 
 
 def test_capacity_table(golden_dir):
@@ -51,22 +51,22 @@ def test_capacity_table(golden_dir):
     budget = g["budget_gib"] * GIB
     for r in g["rows"]:
         n = r["context"]
-        mha = cf.kv_cache_bytes(60, 128, 128, n)
-        gqa = cf.kv_cache_bytes(60, 8, 128, n)
-        mla = cf.mla_cache_bytes(60, 512, 64, n)
+        mha = cf.kv_cache_size(60, 128, 128, n)
+        gqa = cf.kv_cache_size(60, 8, 128, n)
+        mla = cf.latent_cache_size(60, 512, 64, n)
         assert round(mha / GIB, 2) == pytest.approx(r["mha_gib"])
         assert round(gqa / GIB, 2) == pytest.approx(r["gqa8_gib"])
         assert round(mla / GIB, 2) == pytest.approx(r["mla_gib"])
         assert cf.seqs_in_budget(mla, budget) == r["mla_seqs"]
     s = g["seqs_at_32k"]
     n = 32768
-    assert cf.seqs_in_budget(cf.kv_cache_bytes(60, 128, 128, n), budget) == s["mha"]
-    assert cf.seqs_in_budget(cf.kv_cache_bytes(60, 8, 128, n), budget) == s["gqa8"]
-    assert cf.seqs_in_budget(cf.mla_cache_bytes(60, 512, 64, n), budget) == s["mla"]
+    assert cf.seqs_in_budget(cf.kv_cache_size(60, 128, 128, n), budget) == s["mha"]
+    assert cf.seqs_in_budget(cf.kv_cache_size(60, 8, 128, n), budget) == s["gqa8"]
+    assert cf.seqs_in_budget(cf.latent_cache_size(60, 512, 64, n), budget) == s["mla"]
     c = g["cache_at_32768_batch1_gib"]
-    assert round(cf.kv_cache_bytes(60, 128, 128, n) / GIB, 2) == c["mha"]
-    assert round(cf.kv_cache_bytes(60, 8, 128, n) / GIB, 2) == c["gqa8"]
-    assert round(cf.mla_cache_bytes(60, 512, 64, n) / GIB, 2) == c["mla"]
+    assert round(cf.kv_cache_size(60, 128, 128, n) / GIB, 2) == c["mha"]
+    assert round(cf.kv_cache_size(60, 8, 128, n) / GIB, 2) == c["gqa8"]
+    assert round(cf.latent_cache_size(60, 512, 64, n) / GIB, 2) == c["mla"]
 
 
 def test_parameter_counts_fix_weight_layout(golden_dir):
@@ -109,7 +109,7 @@ def test_reduction_claims(golden_dir):
     comparison table is checked."""
     r = _load(golden_dir, "page1_params_and_macs.json")["reduction_claim"]
     assert round(100.0 - r["reduction_pct"], 1) == r["remaining_pct"]
-    ds = 1.0 - cf.mla_cache_bytes(60, 512, 64, 1) / cf.kv_cache_bytes(60, 128, 128, 1)
-    ll = 1.0 - cf.mla_cache_bytes(32, 512, 64, 1) / cf.kv_cache_bytes(32, 32, 128, 1)
+    ds = 1.0 - cf.latent_cache_size(60, 512, 64, 1) / cf.kv_cache_size(60, 128, 128, 1)
+    ll = 1.0 - cf.latent_cache_size(32, 512, 64, 1) / cf.kv_cache_size(32, 32, 128, 1)
     assert round(100 * ds, 2) == 98.24
     assert round(100 * ll, 2) == 92.97

@@ -83,3 +83,25 @@ def test_array_encoder_is_the_scalar_definition():
     assert np.array_equal(got, want)
     assert np.array_equal(fp8.dequantize_row(np.arange(256, dtype=np.uint8), 3)[:0x7F],
                           np.array([fp8.e4m3_decode(c) * 8.0 for c in range(0x7F)]))
+
+
+def test_fp8_rows_quantizes_only_the_latent():
+    """A hand-built row with d_c = 4 and a 2-wide rope block.  max|c| = 500
+    needs e = 1 (448 < 500 <= 896); c * 2^-1 = (0.5, -1.75, 0.15, 250):
+    0.5 and -1.75 are codes, 0.15 lies between 0.140625 and 0.15625 (spacing
+    2^-6 in [1/8, 1/4)) and rounds up, 250 lies between 240 and 256 (spacing
+    16 in [128, 256)) and rounds up.  The rope part comes back unchanged
+    ("Multi-head Latent Attention and KV Cache Compression", section "Moving
+    a trained MHA model over": it is the latent that is quantized further)."""
+    row = np.array([[1.0, -3.5, 0.3, 500.0, 0.123456789, -7.7]])
+    got = fp8.fp8_rows(row, 4)
+    assert got[0, :4].tolist() == [1.0, -3.5, 0.3125, 512.0]
+    assert got[0, 4:].tobytes() == row[0, 4:].tobytes()
+    # a second row with a different scale leaves the first alone
+    rows = np.vstack([row, [[0.001, 0.0, -0.002, 0.0015, 3.0, 4.0]]])
+    got2 = fp8.fp8_rows(rows, 4)
+    assert got2[0].tobytes() == got[0].tobytes()
+    codes, e = fp8.quantize_row(rows[1, :4])
+    assert got2[1, :4].tolist() == fp8.dequantize_row(codes, e).tolist()
+    assert got2[1, 4:].tolist() == [3.0, 4.0]
+    assert rows[0, 2] == 0.3   # the input is not modified in place

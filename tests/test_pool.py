@@ -52,7 +52,7 @@ def test_capacity_against_closed_forms(mla, budget_gib, context, page_size):
     """Whole pages per sequence: the closed form at the page-rounded context."""
     cfg = _dsv2(mla, page_size)
     rounded = -(-context // page_size) * page_size
-    want = cf.seqs_in_budget(cf.mla_cache_bytes(60, 512, 64, rounded), budget_gib * GIB)
+    want = cf.seqs_in_budget(cf.latent_cache_size(60, 512, 64, rounded), budget_gib * GIB)
     assert mla.mla_plan_max_sequences(cfg, 60, budget_gib * GIB, context) == want
 
 
