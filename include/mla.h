@@ -130,6 +130,17 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
 
 void mla_layer_free(mla_layer* layer);
 
+/* Rows of queries x heads one split-KV workgroup attends to in bf16 decode
+ * of a layer with rows in the layer dtype: 0 (default) chooses by shape, 64
+ * or 128 forces that kernel where it applies (128 needs more than 64 rows
+ * per sequence).  Both kernels compute the same attention ("Absorption: the
+ * part that makes it free": scores against the cached rows, weights times
+ * the latent); the choice moves only rounding and speed.  The split plan of
+ * every later decode call of this layer follows it.  Not thread-safe against
+ * decode calls of the same layer.  Errors: INVALID_ARG (null layer, another
+ * value). */
+mla_status mla_layer_set_attention_rows(mla_layer* layer, int32_t rows);
+
 /* Bytes one token occupies in the cache: (d_c + d_rope) * sizeof(dtype)
  * ("The one formula": one latent plus one position key per token and layer,
  * independent of the head count); 644 for MLA_CACHE_FP8 (512 codes, 128

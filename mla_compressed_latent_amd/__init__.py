@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "MlaError", "MlaConfig", "Layer", "LIB_PATH", "lib",
-    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
+    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_layer_set_attention_rows",
+    "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
     "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
     "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
@@ -41,7 +42,8 @@ MLA_OUTPUT_AUTO, MLA_OUTPUT_UNFOLDED, MLA_OUTPUT_FOLDED = 0, 1, 2
 MLA_QUERY_AUTO, MLA_QUERY_UNFOLDED, MLA_QUERY_FOLDED = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
-    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_cache_bytes_per_token",
+    "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_layer_set_attention_rows",
+    "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
     "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_extend_choose_path",
     "mla_extend_workspace_bytes", "mla_extend", "mla_plan_cache", "mla_plan_max_sequences",
@@ -109,6 +111,7 @@ def _load():
         "mla_folded_bytes": (S, [cfgp]),
         "mla_fold_weights": (I32, [cfgp, P, P, P, P, S, P, ctypes.POINTER(P)]),
         "mla_layer_free": (None, [P]),
+        "mla_layer_set_attention_rows": (I32, [P, I32]),
         "mla_cache_bytes_per_token": (S, [cfgp]),
         "mla_append_workspace_bytes": (S, [P, I32]),
         "mla_append_latent": (I32, [P, P, P, P, P, I32, I32, I32, P, I64, P, S, P]),
@@ -253,6 +256,11 @@ def mla_layer_free(layer: Layer):
     if layer.handle:
         lib.mla_layer_free(layer.handle)
         layer.handle = None
+
+
+def mla_layer_set_attention_rows(layer: Layer, rows: int):
+    """Split-KV rows per workgroup for later decode calls: 0 by shape, 64 or 128."""
+    _check(lib.mla_layer_set_attention_rows(layer.handle, int(rows)), "mla_layer_set_attention_rows")
 
 
 def mla_append_workspace_bytes(layer: Layer, total_new: int) -> int:

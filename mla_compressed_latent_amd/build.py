@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip",
+SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip", "splitkv_r128.hip",
            "extend.hip", "project.hip", "pool.cpp"]
 
 HIPCC_FLAGS = [

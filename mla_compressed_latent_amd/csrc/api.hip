@@ -27,6 +27,7 @@ struct mla_layer {
   int out_form = 0;      // MLA_OUTPUT_UNFOLDED or MLA_OUTPUT_FOLDED once folded
   void* wq_p = nullptr;  // query projection, tiled (mla_fold_query)
   int q_form = 0;        // MLA_QUERY_UNFOLDED or MLA_QUERY_FOLDED once folded
+  int attn_rows = 0;     // split-KV rows per workgroup: 0 = by shape, 64 or 128
 };
 
 namespace {
@@ -118,36 +119,44 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
                mla::SplitPlan* p) {
   const int H = L->cfg.num_attention_heads;
   const int rows = max_q_len * H;
-  if (L->elem == 2) {
-    // more than 32 rows: 64-row workgroups of eight waves; else one 32-row block
-    if (rows > 32) {
-      p->NB = 8;
-      p->RQ = (rows + 63) / 64;
-    } else {
-      p->NB = 1;
-      p->RQ = 1;
-    }
-  } else {
-    p->NB = 1;
-    p->RQ = 1;
-  }
-  if (kv_chunk > 0) {
-    if (kv_chunk % 64 || kv_chunk > 8192) return false;
-    p->chunk = kv_chunk;
-  } else {
-    // One resident workgroup per compute unit: cover the longest sequences
-    // with about one wave of workgroups, up to the kernels' largest split
-    // (a batch of 256 ragged sequences of up to 32k tokens measured 2.55 ms
-    // per step at 8192-token splits, 2.65 at 4096, 2.9 at 2048: fewer splits
-    // to merge outweigh the coarser balance).
-    const double target = (double)L->num_cus;
-    const double work = (double)batch * p->RQ * max_seq_len;
-    long c = (long)ceil(work / target);
+  if (kv_chunk > 0 && (kv_chunk % 64 || kv_chunk > 8192)) return false;
+  // One resident workgroup per compute unit: cover the longest sequences
+  // with about one wave of workgroups, up to the kernels' largest split (a
+  // batch of 256 ragged sequences of up to 32k tokens measured 2.55 ms per
+  // step at 8192-token splits, 2.65 at 4096, 2.9 at 2048: fewer splits to
+  // merge outweigh the coarser balance).
+  auto chunk_for = [&](int rq) {
+    if (kv_chunk > 0) return kv_chunk;
+    const double work = (double)batch * rq * max_seq_len;
+    long c = (long)ceil(work / (double)L->num_cus);
     c = ((c + 63) / 64) * 64;
     if (c < 256) c = 256;
     if (c > 8192) c = 8192;
-    p->chunk = (int)c;
+    return (int)c;
+  };
+  p->NB = 1;
+  p->RQ = 1;
+  if (L->elem == 2 && rows > 32) {
+    // more than 32 rows: 64-row workgroups of eight waves, or (bf16 pages,
+    // more than 64 rows) 128-row workgroups of four waves.  The 128-row
+    // kernel's loop is the faster one per row, but its start (query rows and
+    // first tiles) and its write-out are longer and it takes twice the splits
+    // of the 64-row kernel: by shape it is taken for splits of 1024 tokens or
+    // more (measured, DeepSeek-V2 shape: 512-token splits at B32 x 4096, 60
+    // vs 52 us; 4096-token splits at B8 x 128k, 345 vs 375 us).
+    const bool r128_ok = rows > 64 && L->cfg.cache_format == MLA_CACHE_DTYPE;
+    bool use128 = r128_ok && chunk_for((rows + 127) / 128) >= 1024;
+    if (L->attn_rows == 128) use128 = r128_ok;
+    if (L->attn_rows == 64) use128 = false;
+    if (use128) {
+      p->NB = 128;
+      p->RQ = (rows + 127) / 128;
+    } else {
+      p->NB = 8;
+      p->RQ = (rows + 63) / 64;
+    }
   }
+  p->chunk = chunk_for(p->RQ);
   p->S_max = (max_seq_len + p->chunk - 1) / p->chunk;
   return p->S_max <= 1024;   // split weights of one row are staged on chip
 }
@@ -265,12 +274,13 @@ void decode_launch(const mla_layer* L, const void* q, const int32_t* cu_q, const
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
                         c.cache_format == MLA_CACHE_FP8, st);
   if (phases & MLA_PHASE_OUTPUT) {
+    const bool part_bf16 = p.NB == 128;   // the 128-row kernel writes bf16 partials
     if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
-      mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
+      mla::launch_combine_out(p, opart, part_bf16, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
                               c.v_head_dim, L->num_cus, st);
     } else {
-      mla::launch_combine(L->elem, p, opart, lse, cu_q, seq_lens, batch, total_q, H, c.kv_lora_rank,
-                          olat, st);
+      mla::launch_combine(L->elem, p, opart, part_bf16, lse, cu_q, seq_lens, batch, total_q, H,
+                          c.kv_lora_rank, olat, st);
       mla::launch_out_proj(L->elem, olat, L->wuv_p, out, total_q, H, c.kv_lora_rank, c.v_head_dim,
                            st);
     }
@@ -373,6 +383,14 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
 }
 
 void mla_layer_free(mla_layer* layer) { delete layer; }
+
+mla_status mla_layer_set_attention_rows(mla_layer* L, int32_t rows) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  if (rows != 0 && rows != 64 && rows != 128)
+    return fail(MLA_ERR_INVALID_ARG, "mla_layer_set_attention_rows: rows must be 0, 64 or 128 (got %d)", rows);
+  L->attn_rows = rows;
+  return MLA_OK;
+}
 
 size_t mla_append_workspace_bytes(const mla_layer* L, int32_t total_new) {
   if (!L || total_new < 0) return 0;
@@ -695,7 +713,7 @@ mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* 
     mla::SplitPlan p;
     make_plan(L, batch, max_q_len, max_seq_len, 0, &p);
     const DecodeLayout d = decode_layout(L, total_q, p);
-    mla::launch_combine(L->elem, p, (const float*)(ws + d.off_opart), (const float*)(ws + d.off_lse), cu_q,
+    mla::launch_combine(L->elem, p, ws + d.off_opart, p.NB == 128, (const float*)(ws + d.off_lse), cu_q,
                         seq_lens, batch, total_q, c.num_attention_heads, c.kv_lora_rank, ws + d.off_olat, st);
     act = ws + d.off_olat;
   }

@@ -250,9 +250,9 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 constexpr int kCombThreads = 512;
 constexpr int kCombRowPad = 8;   // bf16 pad per LDS row of o_lat
 
-template <int TB>
+template <int TB, typename P>
 __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
-    const float* __restrict__ opart, const float* __restrict__ lse, const int32_t* __restrict__ cu_q,
+    const P* __restrict__ opart, const float* __restrict__ lse, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const bf16* __restrict__ wuv, bf16* __restrict__ out,
     int batch, int Tq, int H, int dv, int chunk, int S_max) {
   static_assert(TB == 32 || TB == 16 || TB == 8 || TB == 4, "token block");
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   constexpr int kSp = 16 / kRows;                        // splits per round of loads
   const int j = 4 * (tid & 127), r0 = tid >> 7;
   f32x4 oacc[kRows];
-  const float* src[kRows];
+  const P* src[kRows];
 #pragma unroll
   for (int u = 0; u < kRows; ++u) {
     oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
 #pragma unroll
       for (int u = 0; u < kRows; ++u)
         if (sp0 + d < sb[u])
-          v[d][u] = *reinterpret_cast<const f32x4*>(src[u] + (sp0 + d) * rows_total * kDc);
+          v[d][u] = load4_f32(src[u] + (sp0 + d) * rows_total * kDc);
   };
   load_round(0);
 
@@ -585,7 +585,7 @@ void launch_out_proj(int elem, const void* olat, const void* wuv, void* out, int
   }
 }
 
-void launch_combine_out(const SplitPlan& plan, const float* opart, const float* lse,
+void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
                         const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
                         int batch, int Tq, int H, int dv, int num_cus, hipStream_t st) {
   // the largest token block that still gives every compute unit a workgroup
@@ -595,9 +595,14 @@ void launch_combine_out(const SplitPlan& plan, const float* opart, const float* 
   switch (TB) {
 #define MLA_COMBINE_CASE(N)                                                                     \
   case N:                                                                                       \
-    combine_out_bf16_kernel<N><<<blocks, kCombThreads, 0, st>>>(                                \
-        opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H, dv, plan.chunk, \
-        plan.S_max);                                                                            \
+    if (part_bf16)                                                                              \
+      combine_out_bf16_kernel<N, bf16><<<blocks, kCombThreads, 0, st>>>(                        \
+          (const bf16*)opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H,  \
+          dv, plan.chunk, plan.S_max);                                                          \
+    else                                                                                        \
+      combine_out_bf16_kernel<N, float><<<blocks, kCombThreads, 0, st>>>(                       \
+          (const float*)opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H, \
+          dv, plan.chunk, plan.S_max);                                                          \
     break;
     MLA_COMBINE_CASE(32) MLA_COMBINE_CASE(16) MLA_COMBINE_CASE(8) MLA_COMBINE_CASE(4)
 #undef MLA_COMBINE_CASE

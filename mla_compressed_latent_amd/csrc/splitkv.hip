@@ -477,8 +477,8 @@ __global__ __launch_bounds__(256) void splitkv_f32_kernel(
 // merges four consecutive latent elements across the splits.
 constexpr int kMaxSplits = 1024;
 
-template <typename T>
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ opart,
+template <typename T, typename P>
+__global__ __launch_bounds__(128) void combine_kernel(const P* __restrict__ opart,
                                                       const float* __restrict__ lse,
                                                       const int32_t* __restrict__ cu_q,
                                                       const int32_t* __restrict__ seq_lens,
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   for (int j = 4 * threadIdx.x; j < dc; j += 4 * blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S_b; ++s) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(opart + (s * rows_total + rowg) * dc + j);
+      const f32x4 v = load4_f32(opart + (s * rows_total + rowg) * dc + j);
       acc += w_s[s] * v;
     }
 #pragma unroll
@@ -536,6 +536,10 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
                           page_size, opart, lse, fp8, st);
         break;
+      case 128:
+        launch_splitkv_r128(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
+                            page_size, opart, lse, st);
+        break;
       default:
         if (fp8)
           splitkv_bf16_kernel<1, true><<<nblocks, 256, 0, st>>>(
@@ -556,15 +560,19 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
   }
 }
 
-void launch_combine(int elem, const SplitPlan& plan, const float* opart, const float* lse,
+void launch_combine(int elem, const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,
                     void* olat, hipStream_t st) {
   const unsigned rows = (unsigned)((int64_t)Tq * H);
   if (elem == 2)
-    combine_kernel<bf16><<<rows, 128, 0, st>>>(opart, lse, cu_q, seq_lens, batch, Tq, H, dc,
+    if (part_bf16)
+      combine_kernel<bf16, bf16><<<rows, 128, 0, st>>>((const bf16*)opart, lse, cu_q, seq_lens, batch, Tq,
+                                                       H, dc, plan.chunk, (bf16*)olat);
+    else
+      combine_kernel<bf16, float><<<rows, 128, 0, st>>>((const float*)opart, lse, cu_q, seq_lens, batch, Tq, H, dc,
                                                plan.chunk, (bf16*)olat);
   else
-    combine_kernel<float><<<rows, 128, 0, st>>>(opart, lse, cu_q, seq_lens, batch, Tq, H, dc,
+    combine_kernel<float, float><<<rows, 128, 0, st>>>((const float*)opart, lse, cu_q, seq_lens, batch, Tq, H, dc,
                                                 plan.chunk, (float*)olat);
 }
 

@@ -51,9 +51,13 @@ def _check(case: GpuCase, out: torch.Tensor, seqs=None, heads=None, tag=""):
     return worst
 
 
-def _run(wl, kv_chunk=0, **kw):
-    print(f"[parity] case {wl.name} B={wl.batch} kv_chunk={kv_chunk}", flush=True)
+def _run(wl, kv_chunk=0, rows=0):
+    """rows: split-KV rows per workgroup (0 by shape; 64 or 128 forces that kernel)."""
+    import mla_compressed_latent_amd as mla
+    print(f"[parity] case {wl.name} B={wl.batch} kv_chunk={kv_chunk} rows={rows}", flush=True)
     case = GpuCase(wl)
+    if rows:
+        mla.mla_layer_set_attention_rows(case.layer, rows)
     case.append_new()
     out = case.decode(kv_chunk=kv_chunk)
     torch.cuda.synchronize()
@@ -77,18 +81,28 @@ SMALL_DSV2 = dataclasses.replace(DSV2, d_model=512)
 SMALL_LLAMA = dataclasses.replace(LLAMA2_7B_MLA, d_model=512)
 
 
+@pytest.mark.parametrize("rows", [64, 128])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 192])
-def test_bf16_dsv2_hidden_prefix(kv_chunk):
+def test_bf16_dsv2_hidden_prefix(kv_chunk, rows):
     wl = workload("dsv2_b32_ctx4096", name="dsv2_small", shape=SMALL_DSV2, batch=3, fixed_prefix=None,
                   max_prefix=700)
-    case, out = _run(wl, kv_chunk=kv_chunk)
-    _check(case, out, tag=f"dsv2_small chunk={kv_chunk}")
+    case, out = _run(wl, kv_chunk=kv_chunk, rows=rows)
+    _check(case, out, tag=f"dsv2_small chunk={kv_chunk} rows={rows}")
 
 
-def test_bf16_dsv2_ragged_paged_two_queries():
+@pytest.mark.parametrize("rows", [64, 128])
+def test_bf16_dsv2_ragged_paged_two_queries(rows):
     wl = workload("dsv2_ragged_paged_256", name="dsv2_ragged_small", batch=7, max_prefix=400)
-    case, out = _run(wl, kv_chunk=128)
-    _check(case, out, tag="dsv2_ragged_small")
+    case, out = _run(wl, kv_chunk=128, rows=rows)
+    _check(case, out, tag=f"dsv2_ragged_small rows={rows}")
+
+
+def test_attention_rows_override_is_validated():
+    import mla_compressed_latent_amd as mla
+    case = GpuCase(workload("dsv2_b32_ctx4096", name="rows_arg", shape=SMALL_DSV2, batch=1, fixed_prefix=16))
+    for bad in (-1, 32, 96, 256):
+        with pytest.raises(mla.MlaError):
+            mla.mla_layer_set_attention_rows(case.layer, bad)
 
 
 def test_bf16_llama_shape():
@@ -106,13 +120,14 @@ def test_bf16_llama_two_queries_paged():
     _check(case, out, tag="llama_q2")
 
 
-def test_minimal_contexts():
+@pytest.mark.parametrize("rows", [64, 128])
+def test_minimal_contexts(rows):
     """Context 1 (one query on its own row) and context 2 with two queries."""
     for q_len in (1, 2):
         wl = workload("dsv2_ragged_paged_256", name=f"minimal_q{q_len}", batch=2, fixed_prefix=0,
                       fixed_q_len=q_len)
-        case, out = _run(wl)
-        _check(case, out, tag=f"minimal q_len={q_len}")
+        case, out = _run(wl, rows=rows)
+        _check(case, out, tag=f"minimal q_len={q_len} rows={rows}")
 
 
 def test_deterministic_and_page_permutation_invariant():
@@ -140,19 +155,25 @@ def test_deterministic_and_page_permutation_invariant():
 
 
 def test_split_invariance():
+    import mla_compressed_latent_amd as mla
     wl = workload("dsv2_b32_ctx4096", name="splits", shape=SMALL_DSV2, batch=2, fixed_prefix=1000)
     case, out_a = _run(wl, kv_chunk=64)
     out_b = case.decode(kv_chunk=1024)
     out_c = case.decode(kv_chunk=0)
+    mla.mla_layer_set_attention_rows(case.layer, 128)
+    out_d = case.decode(kv_chunk=64)
+    out_e = case.decode(kv_chunk=1024)
     torch.cuda.synchronize()
-    a, b, c = (o.float().cpu().numpy() for o in (out_a, out_b, out_c))
+    a, *rest = (o.float().cpu().numpy() for o in (out_a, out_b, out_c, out_d, out_e))
     scale = np.abs(a).max()
-    assert np.abs(a - b).max() / scale < 1e-2 and np.abs(a - c).max() / scale < 1e-2
+    for r in rest:
+        assert np.abs(a - r).max() / scale < 1e-2
 
 
 def test_many_splits_separate_combine():
     """More splits than the fused combine stages (64): the separate combine and
     output-projection kernels run instead; sampled heads against the oracle."""
+    import mla_compressed_latent_amd as mla
     wl = workload("dsv2_b32_ctx4096", name="many_splits", shape=SMALL_DSV2, batch=2, fixed_prefix=4500)
     case, out = _run(wl, kv_chunk=64)
     heads = [0, 37, 127]
@@ -160,18 +181,23 @@ def test_many_splits_separate_combine():
     out_fused = case.decode(kv_chunk=128)     # 36 splits: fused combine + projection
     torch.cuda.synchronize()
     _check(case, out_fused, heads=heads, tag="many_splits chunk=128 (36 splits)")
+    mla.mla_layer_set_attention_rows(case.layer, 128)   # bf16 partials of the 128-row kernel
+    for chunk in (64, 128):
+        out128 = case.decode(kv_chunk=chunk)
+        torch.cuda.synchronize()
+        _check(case, out128, heads=heads, tag=f"many_splits chunk={chunk} rows=128")
 
 
 def test_split_plan_of_the_benchmarked_shapes():
     """The planner's split sizes for the benchmarked decode shapes on a
-    256-CU MI355X (chosen by measurement: one wave of workgroups, splits up
-    to 8192 tokens)."""
+    256-CU MI355X (one wave of workgroups, splits up to 8192 tokens; 128-row
+    workgroups where their split reaches 1024 tokens, 64-row ones else)."""
     import mla_compressed_latent_amd as mla
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("split sizes are stated for 256 compute units")
     cases = [  # (shape, batch, max_q_len, max_seq_len, expected tokens per split)
         (SMALL_DSV2, 32, 1, 4096, 1024),
-        (SMALL_DSV2, 8, 1, 131072, 8192),
+        (SMALL_DSV2, 8, 1, 131072, 4096),
         (SMALL_DSV2, 256, 2, 32770, 8192),
         (SMALL_LLAMA, 64, 1, 8192, 2048),
     ]
