@@ -207,6 +207,28 @@ mla_status mla_decode(const mla_layer* layer, const void* q, const int32_t* cu_q
                       int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Size of the device scratch mla_decode_no_alloc works in (64 MiB per GPU). */
+#define MLA_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Same arguments and results as mla_decode; the
+ * workspace is a static device array of MLA_NO_ALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, looked up on
+ * the first call on the current device (which must own q, cache, out and
+ * hip_stream).  Nothing is allocated, and nothing in the scratch has to
+ * start at zero.  All calls on one GPU share its array: calls that overlap
+ * in time on one GPU (two streams, two threads) race and give wrong results;
+ * serialize them (one stream).  Errors: as mla_decode, plus
+ * INSUFFICIENT_WORKSPACE when mla_decode_workspace_bytes for these bounds
+ * exceeds MLA_NO_ALLOC_SCRATCH_BYTES (fewer splits -- a larger kv_chunk -- or
+ * a smaller batch fit), HIP if the scratch cannot be found on the device. */
+mla_status mla_decode_no_alloc(const mla_layer* layer, const void* q, const int32_t* cu_q,
+                               const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                               int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                               int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
+                               void* hip_stream);
+
 /* The three phases of mla_decode, for callers that interleave their own
  * work between them (timing, other streams):
  *   MLA_PHASE_ABSORB  fold each query into latent space and rotate its rope

@@ -19,7 +19,8 @@ __all__ = [
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_layer_set_attention_rows",
     "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
-    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_status_string", "mla_last_error",
+    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_decode_no_alloc",
+    "MLA_NO_ALLOC_SCRATCH_BYTES", "mla_status_string", "mla_last_error",
     "config_from_shape", "EXPORTED_SYMBOLS", "MLA_PHASE_ABSORB", "MLA_PHASE_ATTEND", "MLA_PHASE_OUTPUT",
     "MLA_PHASE_ALL", "mla_extend_choose_path", "mla_extend_workspace_bytes", "mla_extend",
     "MLA_EXTEND_AUTO", "MLA_EXTEND_ABSORBED", "MLA_EXTEND_EXPANDED",
@@ -40,12 +41,14 @@ MLA_EXTEND_AUTO, MLA_EXTEND_ABSORBED, MLA_EXTEND_EXPANDED = 0, 1, 2
 MLA_CACHE_DTYPE, MLA_CACHE_FP8 = 0, 1
 MLA_OUTPUT_AUTO, MLA_OUTPUT_UNFOLDED, MLA_OUTPUT_FOLDED = 0, 1, 2
 MLA_QUERY_AUTO, MLA_QUERY_UNFOLDED, MLA_QUERY_FOLDED = 0, 1, 2
+MLA_NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED_SYMBOLS = (
     "mla_folded_bytes", "mla_fold_weights", "mla_layer_free", "mla_layer_set_attention_rows",
     "mla_cache_bytes_per_token",
     "mla_append_workspace_bytes", "mla_append_latent", "mla_decode_kv_chunk",
-    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_extend_choose_path",
+    "mla_decode_workspace_bytes", "mla_decode", "mla_decode_phases", "mla_decode_no_alloc",
+    "mla_extend_choose_path",
     "mla_extend_workspace_bytes", "mla_extend", "mla_plan_cache", "mla_plan_max_sequences",
     "mla_pool_create", "mla_pool_destroy", "mla_pool_reserve", "mla_pool_release", "mla_pool_free_pages",
     "mla_pool_length", "mla_pool_page_table", "mla_output_choose_form", "mla_output_folded_bytes",
@@ -120,6 +123,7 @@ def _load():
         "mla_decode": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P]),
         "mla_decode_phases": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S, P,
                                     ctypes.c_uint32]),
+        "mla_decode_no_alloc": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P]),
         "mla_decode_step_workspace_bytes": (S, [P, I32, I32, I32, I32, I32, I32]),
         "mla_decode_step": (I32, [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I64, P, P, S,
                                   P]),
@@ -318,6 +322,18 @@ def mla_decode_phases(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, m
         int(max_seq_len), int(kv_chunk), _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(out, "out", dt),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream),
         int(phases)), "mla_decode")
+
+
+def mla_decode_no_alloc(layer: Layer, q, cu_q, seq_lens, page_table, cache, out, max_q_len: int,
+                        max_seq_len: int, kv_chunk: int = 0, stream=None):
+    """mla_decode in the library's static device scratch: allocates nothing (see include/mla.h)."""
+    dt = layer.cfg.torch_dtype
+    _check(lib.mla_decode_no_alloc(
+        layer.handle, _dev(q, "q", dt), _dev(cu_q, "cu_q", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(page_table, "page_table", torch.int32), int(page_table.shape[1]), int(seq_lens.shape[0]),
+        int(q.shape[0]), int(max_q_len), int(max_seq_len), int(kv_chunk),
+        _dev(cache, "cache", layer.cfg.cache_torch_dtype), int(cache.shape[0]), _dev(out, "out", dt),
+        _stream(stream)), "mla_decode_no_alloc")
 
 
 def mla_decode_step_workspace_bytes(layer: Layer, batch: int, total_new: int, total_q: int, max_q_len: int,

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -172,7 +174,8 @@ DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan
   DecodeLayout d;
   d.off_abuf = 0;
   d.off_opart = align256(rows * D * L->elem);
-  d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * 4);
+  const size_t part_elem = p.NB == 128 ? 2 : 4;   // the 128-row kernel writes bf16 partials
+  d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * part_elem);
   d.off_olat = d.off_lse + align256((size_t)p.S_max * rows * 4);
   d.total = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
   return d;
@@ -301,6 +304,46 @@ void append_finish(const mla_layer* L, const float* part, const int32_t* cu_new,
     mla::launch_append_finish(L->elem, part, ks, total_new, cu_new, prefix_lens, page_table, max_pages,
                               batch, cache, c.page_size, c.kv_lora_rank, c.qk_rope_head_dim, c.rope_base,
                               L->freq, st);
+}
+
+}  // namespace
+
+// Scratch of mla_decode_no_alloc: its decode workspace, one copy per GPU,
+// resident from the library's load on that GPU to the process end.  Host
+// code never passes this name to a kernel (on the host it is only a
+// stand-in); it uses the device address looked up once per device.
+static __device__ __align__(256) char scratch[MLA_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (nullptr + g_err on error).
+char* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(MLA_ERR_HIP, "mla_decode_no_alloc: no usable current device (%d)", dev);
+    return nullptr;
+  }
+  char* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !addr) {
+    (void)hipGetLastError();
+    fail(MLA_ERR_HIP, "mla_decode_no_alloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  ptr = (char*)addr;
+  g_scratch_dev[dev].store(ptr, std::memory_order_release);
+  return ptr;
 }
 
 }  // namespace
@@ -471,6 +514,31 @@ mla_status mla_decode(const mla_layer* L, const void* q, const int32_t* cu_q, co
   return mla_decode_phases(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
                            max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
                            hip_stream, MLA_PHASE_ALL);
+}
+
+mla_status mla_decode_no_alloc(const mla_layer* L, const void* q, const int32_t* cu_q,
+                               const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages,
+                               int32_t batch, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                               int32_t kv_chunk, const void* cache, int64_t num_pages, void* out,
+                               void* hip_stream) {
+  if (!L) return fail(MLA_ERR_INVALID_ARG, "layer is null");
+  const size_t need = mla_decode_workspace_bytes(L, batch, total_q, max_q_len, max_seq_len, kv_chunk);
+  if (need > MLA_NO_ALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_INSUFFICIENT_WORKSPACE,
+                "mla_decode_no_alloc: this call needs %zu bytes of scratch, the static buffer holds %zu; "
+                "use mla_decode with a workspace",
+                need, (size_t)MLA_NO_ALLOC_SCRATCH_BYTES);
+  char* ws = scratch_address();
+  if (!ws) return MLA_ERR_HIP;
+  mla::SplitPlan p;
+  DecodeLayout d;
+  const mla_status s = decode_prepare(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                                      max_seq_len, kv_chunk, cache, num_pages, out, ws,
+                                      MLA_NO_ALLOC_SCRATCH_BYTES, &p, &d);
+  if (s != MLA_OK) return s;
+  decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p, d,
+                MLA_PHASE_ALL, (hipStream_t)hip_stream);
+  return hip_check("decode launch");
 }
 
 size_t mla_decode_step_workspace_bytes(const mla_layer* L, int32_t batch, int32_t total_new,
