@@ -375,6 +375,38 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def run_phase(st, r, phase):
+    """One decode phase (mla_decode_phases) on rotated copy r."""
+    mla = st["mla"]
+    mla.mla_decode_phases(st["layers"][r], st["q"], st["cu_q"], st["seq_lens"], st["table"], st["caches"][r],
+                          st["out"], st["max_q_len"], st["max_seq_len"], st["kv_chunk"], st["dws"], phases=phase)
+
+
+def graph_phase_us(st, phase, replays):
+    """Average launch time of one decode phase: a HIP graph holding the phase
+    once on each of the R rotated copies, replayed back to back, timed with
+    HIP events on the replay stream (the stream the kernels run on)."""
+    import torch
+    R = st["R"]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for r in range(R):
+                run_phase(st, r, phase)
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * R)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -477,10 +509,17 @@ def main():
     w1.record()
     torch.cuda.synchronize()
     warm_ms_step = w0.elapsed_time(w1) / (max(1, K // R) * R)
+    # The attention kernel and the combine + output kernels on their own:
+    # back-to-back launches in a graph, each on its own cache copy.
+    mla = st["mla"]
+    replays = max(2, K // R)
+    attend_us = graph_phase_us(st, mla.MLA_PHASE_ATTEND, replays)
+    output_us = graph_phase_us(st, mla.MLA_PHASE_OUTPUT, replays)
     s = st["s"]
     latent_bytes = int(st["seq_lens_np"].astype("int64").sum()) * s.cache_token_bytes
-    attend_s = phase[2] * 1e-3
+    attend_s = attend_us * 1e-6
     achieved = latent_bytes / attend_s / 1e9
+    grading = latent_bytes / ((attend_us + output_us) * 1e-6) / 1e9
     # scores (K = d_c + d_rope) and value sums (K = d_c) per query row and cached token
     q_lens = wl.q_lens()
     traffic = MEASURED_TRAFFIC.get((splitkv_source_id(), wl.name))
@@ -519,18 +558,25 @@ def main():
         "attend_us_p10_p50_p90": [pct(attend_each, q) * 1e3 for q in (0.1, 0.5, 0.9)],
         "phase_us": {"append": phase[0] * 1e3, "absorb": phase[1] * 1e3, "attend": phase[2] * 1e3,
                      "combine_and_output": phase[3] * 1e3},
+        "kernel_us": {"attend": attend_us, "combine_and_output": output_us},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_bytes,
             "traffic_detail": traffic,
             "kernel": "split-KV attention (MLA_PHASE_ATTEND)",
+            "timing": ("HIP events around a graph of back-to-back MLA_PHASE_ATTEND launches, one per rotated "
+                       "copy (kernel_us.attend); phase_us are eager event times including launch gaps"),
+            "grading_achieved": grading,
+            "grading_frac": grading / HBM_PEAK_GBPS,
+            "grading": "latent bytes / (split-KV attention + combine and W_uv output), both graph-timed",
             "algorithmic_bytes_per_launch": latent_bytes,
             "mfma_tflops": flops / attend_s / 1e12,
             "mfma_frac_of_bf16_peak": flops / attend_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
     }
     log(f"{ms_step * 1e3:.1f} us/step (graph), {eager_ms * 1e3:.1f} us/step eager, attend "
-        f"{phase[2] * 1e3:.1f} us -> {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak)")
+        f"{attend_us:.1f} us -> {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBPS:.1f}% of HBM peak); "
+        f"attend + output {attend_us + output_us:.1f} us -> {100 * grading / HBM_PEAK_GBPS:.1f}%")
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -42,6 +42,13 @@
  *    (lengths, page ids) are trusted: the caller guarantees
  *    1 <= q_len_b <= seq_len_b <= max_seq_len, q_len_b <= max_q_len and
  *    that every page id a sequence touches lies in [0, num_pages).
+ *  - The checking build (libmla_debug.so, the same sources compiled with
+ *    MLA_DEBUG_CHECKS) verifies those device-resident values before every
+ *    append, decode and extend: one single-workgroup kernel checks each
+ *    sequence's offsets, lengths and page ids, the call waits for it, and a
+ *    failure returns MLA_ERR_INVALID_ARG (mla_last_error() names the first
+ *    bad sequence) with nothing else enqueued.  It synchronises the stream,
+ *    so it does not check calls made while the stream is being captured.
  *  - Positions are 0-based token indices.  Sequence b's cached token t lives
  *    in row (t % page_size) of page page_table[b * max_pages + t / page_size].
  *  - mla_last_error() returns a thread-local message for the last non-OK
@@ -107,7 +114,9 @@ typedef struct {
 typedef struct mla_layer mla_layer; /* opaque host handle */
 
 /* Bytes of the folded-weight buffer mla_fold_weights fills (0 if cfg is
- * invalid or unsupported). */
+ * invalid or unsupported): W_dkv, W_uk and W_uv in the kernels' operand
+ * layouts, the fold that "Absorption: the part that makes it free" does once
+ * at load. */
 size_t mla_folded_bytes(const mla_config* cfg);
 
 /* Fold the layer's weights once at load ("Absorption: the part that makes it
@@ -128,6 +137,8 @@ mla_status mla_fold_weights(const mla_config* cfg, const void* w_dkv, const void
                             const void* w_uv, void* folded, size_t folded_bytes,
                             void* hip_stream, mla_layer** out);
 
+/* Release the host handle made by mla_fold_weights (the folded buffer stays
+ * the caller's).  Null is a no-op. */
 void mla_layer_free(mla_layer* layer);
 
 /* Rows of queries x heads one split-KV workgroup attends to in bf16 decode
@@ -180,11 +191,25 @@ mla_status mla_append_latent(const mla_layer* layer, const void* x, const int32_
 int32_t mla_decode_kv_chunk(const mla_layer* layer, int32_t batch, int32_t max_q_len,
                             int32_t max_seq_len, int32_t kv_chunk);
 
-/* Workspace mla_decode needs for these bounds (same kv_chunk meaning). */
+/* Workspace mla_decode needs for these bounds (same kv_chunk meaning): the
+ * absorbed queries, each split's partial output and log-sum-exp, and the
+ * merged latent output, i.e. the intermediate results of the re-associated
+ * attention of "Absorption: the part that makes it free" (0 on invalid
+ * arguments). */
 size_t mla_decode_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t total_q,
                                   int32_t max_q_len, int32_t max_seq_len, int32_t kv_chunk);
 
 /* One absorbed decode step over a paged latent cache.
+ *
+ * Defined by "Multi-head Latent Attention: the KV cache, compressed":
+ * "Absorption: the part that makes it free" (each head's query is folded
+ * through W_uk and scored against the cached latents themselves; the softmax
+ * weights sum the latents, and W_uv is applied to that sum, so no per-head key
+ * or value is formed) and "RoPE, and why the explanations stop here" with
+ * "The code" (decoupled_score: the score adds a position part, the rotated
+ * query rope part against the cached, already rotated, shared rope key); and
+ * by "Multi-head Latent Attention and KV Cache Compression", "The absorption
+ * trick and decoupled RoPE" (one softmax scale over the sum of both parts).
  *
  *   q         [total_q][H][d_nope + d_rope]  device; queries BEFORE rotation;
  *             sequence b owns rows cu_q[b] .. cu_q[b+1]-1
@@ -522,6 +547,10 @@ mla_status mla_decode_hidden(const mla_layer* layer, const void* x, const int32_
                              const void* cache, int64_t num_pages, void* out, void* workspace,
                              size_t workspace_bytes, void* hip_stream);
 
+/* Status bookkeeping (no passage defines it): the name of a status code,
+ * and the calling thread's message for its last non-OK status -- in the
+ * checking build, also which sequence, length or page id failed the check of
+ * device-resident arguments. */
 const char* mla_status_string(mla_status s);
 const char* mla_last_error(void);
 

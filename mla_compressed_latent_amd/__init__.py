@@ -32,7 +32,14 @@ __all__ = [
     "mla_decode_hidden", "MLA_QUERY_AUTO", "MLA_QUERY_UNFOLDED", "MLA_QUERY_FOLDED",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+# MLA_LIBRARY=debug selects the checking build (device-resident lengths and
+# page ids verified before each call's kernels; see include/mla.h).
+LIBRARIES = {"release": os.path.join(_PKG_DIR, "libmla.so"), "debug": os.path.join(_PKG_DIR, "libmla_debug.so")}
+LIB_VARIANT = os.environ.get("MLA_LIBRARY", "release")
+if LIB_VARIANT not in LIBRARIES:
+    raise ImportError(f"MLA_LIBRARY={LIB_VARIANT!r}: expected one of {sorted(LIBRARIES)}")
+LIB_PATH = LIBRARIES[LIB_VARIANT]
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP, MLA_ERR_INSUFFICIENT_WORKSPACE = range(5)
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
@@ -102,12 +109,13 @@ class MlaCachePlan(ctypes.Structure):
     ]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path=None):
+    path = path or LIB_PATH
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python mla_compressed_latent_amd/build.py` "
+            f"{path} is missing: build it with `python mla_compressed_latent_amd/build.py` "
             "(the decode path has no CPU fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     cfgp = ctypes.POINTER(MlaConfig)
     sig = {
@@ -160,6 +168,15 @@ def _load():
 
 
 lib = _load()
+
+
+def use_library(variant: str):
+    """Bind every function of this module to another build of the library
+    ("release" or "debug") from now on.  Handles (layers, pools) made under
+    one build must be released before switching and are not used across."""
+    global lib, LIB_VARIANT, LIB_PATH
+    lib = _load(LIBRARIES[variant])
+    LIB_VARIANT, LIB_PATH = variant, LIBRARIES[variant]
 
 
 def _status_name(s: int) -> str:
@@ -224,11 +241,12 @@ class Layer:
         self.handle = handle
         self.cfg = cfg
         self.folded = folded
+        self._free = lib.mla_layer_free   # the build that made the handle releases it
 
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:
-            lib.mla_layer_free(h)
+            self._free(h)
             self.handle = None
 
 
@@ -258,7 +276,7 @@ def mla_fold_weights(cfg: MlaConfig, w_dkv, w_uk, w_uv, folded=None, stream=None
 
 def mla_layer_free(layer: Layer):
     if layer.handle:
-        lib.mla_layer_free(layer.handle)
+        layer._free(layer.handle)
         layer.handle = None
 
 

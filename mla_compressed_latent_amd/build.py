@@ -23,7 +23,12 @@ LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "pack.hip", "append.hip", "gemm_heads.hip", "splitkv.hip", "splitkv_x8.hip", "splitkv_r128.hip",
-           "extend.hip", "project.hip", "pool.cpp"]
+           "extend.hip", "project.hip", "check.hip", "pool.cpp"]
+# The checking build (libmla_debug.so): the same objects, with api.hip
+# compiled again with MLA_DEBUG_CHECKS (device-resident lengths and page ids
+# verified before each call's kernels run).
+DEBUG_LIB = os.path.join(PKG, "libmla_debug.so")
+DEBUG_SOURCE = "api.hip"
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -45,10 +50,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmla.so)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-           os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_debug.o" if debug else ".o"))
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DMLA_DEBUG_CHECKS=1"] if debug else []), "-I", os.path.join(ROOT, "include"),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,18 +66,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libmla.so and the checking build libmla_debug.so; returns the former's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(DEBUG_SOURCE, True)]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    release = objs[:len(SOURCES)]
+    debug = [objs[-1] if s == DEBUG_SOURCE else o for s, o in zip(SOURCES, release)]
+    _link(release, LIB, verbose)
+    _link(debug, DEBUG_LIB, verbose)
     return LIB
 
 

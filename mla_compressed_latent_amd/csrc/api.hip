@@ -12,25 +12,14 @@
 #include <string>
 
 #include "../../include/mla.h"
+#include "check.hpp"
 #include "kernels.hpp"
+#include "layer.hpp"
 
-struct mla_layer {
-  mla_config cfg;
-  int elem;        // bytes per stored element
-  float scale;     // softmax scale actually used
-  // folded weights: fragment-tiled for bf16, transposed row-major for fp32
-  void* wdkv_t;    // rows n < D, k = d < d_model
-  void* wuk_p;     // per head: rows j < d_c, k = i < d_nope
-  void* wuv_p;     // per head: rows v < d_v, k = j < d_c
-  void* wukt_p;    // bf16: per head, rows i < d_nope, k = j < d_c (expanded path)
-  mla::RopeFreq freq;   // rotary frequencies (bf16 layers)
-  int num_cus;
-  void* wo_p = nullptr;  // output projection, tiled (mla_fold_output)
-  int out_form = 0;      // MLA_OUTPUT_UNFOLDED or MLA_OUTPUT_FOLDED once folded
-  void* wq_p = nullptr;  // query projection, tiled (mla_fold_query)
-  int q_form = 0;        // MLA_QUERY_UNFOLDED or MLA_QUERY_FOLDED once folded
-  int attn_rows = 0;     // split-KV rows per workgroup: 0 = by shape, 64 or 128
-};
+// The checking build compiles this file with -DMLA_DEBUG_CHECKS=1.
+#ifndef MLA_DEBUG_CHECKS
+#define MLA_DEBUG_CHECKS 0
+#endif
 
 namespace {
 
@@ -348,6 +337,74 @@ char* scratch_address() {
 
 }  // namespace
 
+// Result words of the checking build's argument check (launch_check_args).
+static __device__ uint32_t check_result[2];
+
+namespace {
+
+constexpr bool kDebugChecks = MLA_DEBUG_CHECKS != 0;
+std::mutex g_check_mu;
+
+const char* check_code_name(uint32_t code) {
+  switch (code) {
+    case mla_check::kBadOffsets: return "sequence offsets out of order or range";
+    case mla_check::kBadQueryLen: return "query count outside [1, max_q_len]";
+    case mla_check::kBadSeqLen: return "sequence length outside [query count, max_seq_len]";
+    case mla_check::kBadPrefix: return "prefix length negative or beyond the page-table row";
+    case mla_check::kBadPage: return "page id outside [0, num_pages) at page index";
+  }
+  return "unknown check failure";
+}
+
+// Checking build only: run the device check of this call's offsets,
+// lengths and page ids, wait for it, and fail the call if it found a bad
+// sequence.  Not under stream capture (it cannot wait there).  One check at
+// a time per process: the result words are shared.
+mla_status device_check(const char* what, bool append, const int32_t* cu, const int32_t* lens,
+                        const int32_t* page_table, int max_pages, int batch, int total, int max_q_len,
+                        int max_seq_len, int page_size, int64_t num_pages, hipStream_t st) {
+  if (!kDebugChecks) return MLA_OK;
+  auto hip_fail = [&](hipError_t e) {
+    (void)hipGetLastError();
+    return fail(MLA_ERR_HIP, "%s: device argument check: %s", what, hipGetErrorString(e));
+  };
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cs != hipStreamCaptureStatusNone) return MLA_OK;
+  std::lock_guard<std::mutex> lock(g_check_mu);
+  void* addr = nullptr;
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(check_result));
+  if (e != hipSuccess || !addr) return hip_fail(e);
+  mla::launch_check_args(append, cu, lens, page_table, max_pages, batch, total, max_q_len, max_seq_len,
+                         page_size, num_pages, (uint32_t*)addr, st);
+  uint32_t res[2] = {0, 0};
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(res, addr, sizeof res, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (res[0] == mla_check::kNone) return MLA_OK;
+  return fail(MLA_ERR_INVALID_ARG, "%s: device argument check: sequence %d: %s %d", what,
+              mla_check::failed_sequence(res[0]), check_code_name(mla_check::failed_code(res[0])),
+              (int32_t)res[1]);
+}
+
+mla_status device_check_decode(const mla_layer* L, const char* what, const int32_t* cu_q, const int32_t* seq_lens,
+                               const int32_t* page_table, int max_pages, int batch, int total_q, int max_q_len,
+                               int max_seq_len, int64_t num_pages, hipStream_t st) {
+  return device_check(what, false, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                      max_seq_len, L->cfg.page_size, num_pages, st);
+}
+
+mla_status device_check_append(const mla_layer* L, const char* what, const int32_t* cu_new,
+                               const int32_t* prefix_lens, const int32_t* page_table, int max_pages, int batch,
+                               int total_new, int64_t num_pages, hipStream_t st) {
+  return device_check(what, true, cu_new, prefix_lens, page_table, max_pages, batch, total_new, 0, 0,
+                      L->cfg.page_size, num_pages, st);
+}
+
+}  // namespace
+
 // Shared with the host-only parts of the library (pool.cpp).
 namespace mla_api {
 mla_status fail_msg(mla_status s, const char* msg) { return fail(s, "%s", msg); }
@@ -461,6 +518,9 @@ mla_status mla_append_latent(const mla_layer* L, const void* x, const int32_t* c
   const int D = c.kv_lora_rank + c.qk_rope_head_dim;
   hipStream_t st = (hipStream_t)hip_stream;
   float* part = (float*)workspace;
+  const mla_status chk = device_check_append(L, "mla_append_latent", cu_new, prefix_lens, page_table, max_pages,
+                                             batch, total_new, num_pages, st);
+  if (chk != MLA_OK) return chk;
   if (L->elem == 2)
     mla::launch_append_gemm_bf16(x, L->wdkv_t, part, total_new, D, c.d_model, st);
   else
@@ -501,6 +561,9 @@ mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* c
                                       max_seq_len, kv_chunk, cache, num_pages, out, workspace, workspace_bytes,
                                       &p, &d);
   if (s != MLA_OK) return s;
+  const mla_status chk = device_check_decode(L, "mla_decode", cu_q, seq_lens, page_table, max_pages, batch,
+                                             total_q, max_q_len, max_seq_len, num_pages, (hipStream_t)hip_stream);
+  if (chk != MLA_OK) return chk;
   decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out,
                 (char*)workspace, p, d, phases, (hipStream_t)hip_stream);
   return hip_check("decode launch");
@@ -536,6 +599,10 @@ mla_status mla_decode_no_alloc(const mla_layer* L, const void* q, const int32_t*
                                       max_seq_len, kv_chunk, cache, num_pages, out, ws,
                                       MLA_NO_ALLOC_SCRATCH_BYTES, &p, &d);
   if (s != MLA_OK) return s;
+  const mla_status chk = device_check_decode(L, "mla_decode_no_alloc", cu_q, seq_lens, page_table, max_pages,
+                                             batch, total_q, max_q_len, max_seq_len, num_pages,
+                                             (hipStream_t)hip_stream);
+  if (chk != MLA_OK) return chk;
   decode_launch(L, q, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len, cache, out, ws, p, d,
                 MLA_PHASE_ALL, (hipStream_t)hip_stream);
   return hip_check("decode launch");
@@ -576,6 +643,14 @@ mla_status mla_decode_step(const mla_layer* L, const void* x, const int32_t* cu_
   char* ws = (char*)workspace;
   float* part = (float*)(ws + off_app);
   const int D = c.kv_lora_rank + c.qk_rope_head_dim;
+  if (total_new > 0) {
+    s = device_check_append(L, "mla_decode_step", cu_new, prefix_lens, page_table, max_pages, batch, total_new,
+                            num_pages, st);
+    if (s != MLA_OK) return s;
+  }
+  s = device_check_decode(L, "mla_decode_step", cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
+                          max_seq_len, num_pages, st);
+  if (s != MLA_OK) return s;
   uint32_t phases = MLA_PHASE_ALL;
   if (total_new > 0 && L->elem == 2 && c.cache_format == MLA_CACHE_DTYPE) {
     // the append GEMM, then the query absorb with the append finish
@@ -656,6 +731,9 @@ mla_status mla_extend(const mla_layer* L, const void* q, const int32_t* cu_q, co
                 workspace_bytes, e.total);
   if ((uintptr_t)workspace % 256) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t st = (hipStream_t)hip_stream;
+  const mla_status chk = device_check_decode(L, "mla_extend", cu_q, seq_lens, page_table, max_pages, batch,
+                                             total_q, max_q_len, max_seq_len, num_pages, st);
+  if (chk != MLA_OK) return chk;
   char* ws = (char*)workspace;
   const int H = c.num_attention_heads;
   mla::launch_expand_kv(cache, seq_lens, page_table, max_pages, batch, H, c.qk_nope_head_dim, c.v_head_dim,
@@ -894,6 +972,9 @@ mla_status mla_decode_hidden(const mla_layer* L, const void* x, const int32_t* c
   const mla_status s = decode_prepare(L, x, cu_q, seq_lens, page_table, max_pages, batch, total_q, max_q_len,
                                       max_seq_len, 0, cache, num_pages, out, ws, hl.off_q, &p, &d);
   if (s != MLA_OK) return s;
+  const mla_status chk = device_check_decode(L, "mla_decode_hidden", cu_q, seq_lens, page_table, max_pages, batch,
+                                             total_q, max_q_len, max_seq_len, num_pages, st);
+  if (chk != MLA_OK) return chk;
   if (L->q_form == MLA_QUERY_UNFOLDED) {
     // q = x . W_q, then the whole decode from q (its own absorb)
     void* q = ws + hl.off_q;

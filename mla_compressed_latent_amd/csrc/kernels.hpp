@@ -13,6 +13,16 @@ namespace mla {
 // fp32 row scales.
 constexpr int kFp8RowBytes = 640;
 
+// ---- checking build ---------------------------------------------------------
+// One workgroup checks every sequence's device-resident offsets, lengths and
+// page ids (check.hpp; append: cu = cu_new, lens = prefix_lens, total =
+// total_new; else cu = cu_q, lens = seq_lens, total = total_q) and writes
+// result[0] = the first failure's word (mla_check::kNone if none) and
+// result[1] = its detail.
+void launch_check_args(bool append, const int32_t* cu, const int32_t* lens, const int32_t* page_table,
+                       int max_pages, int batch, int total, int max_q_len, int max_seq_len, int page_size,
+                       int64_t num_pages, uint32_t* result, hipStream_t st);
+
 // ---- fold (pack) ---------------------------------------------------------
 // bf16 (elem 2): fragment-tiled wdkv (rows n, k = d), wuk[h] (rows j, k = i),
 // wuv[h] (rows v, k = j), wukt[h] (rows i, k = j).  fp32 (elem 4):

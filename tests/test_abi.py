@@ -23,15 +23,18 @@ def mla():
     return m
 
 
-def test_header_and_exports_agree(mla):
+@pytest.mark.parametrize("variant", ["release", "debug"])
+def test_header_and_exports_agree(mla, variant):
+    """Both builds (release and the checking build) export exactly the header's calls."""
     declared = _declared()
     assert set(declared) == set(mla.EXPORTED_SYMBOLS)
-    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True,
+    path = mla.LIBRARIES[variant]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (mla_[a-z_]+)$", out, flags=re.M))
     assert set(declared) <= exported, set(declared) - exported
     assert exported <= set(declared), f"undeclared exports {exported - set(declared)}"
-    lib = ctypes.CDLL(mla.LIB_PATH)
+    lib = ctypes.CDLL(path)
     for name in declared:
         assert hasattr(lib, name)
 
