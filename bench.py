@@ -37,15 +37,13 @@ EXTEND_METRIC = "MLA chunked-extend / prefill query tokens/s and matrix-core TFL
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("4df1e4b2c223f723", "dsv2_b32_ctx4096"): {"fetch_bytes": 155909588, "write_bytes": 36660335},
-    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606559264, "write_bytes": 16882790},
-    ("4df1e4b2c223f723", "dsv2_b8_ctx131072"): {"fetch_bytes": 1209267458, "write_bytes": 35948877},
-    ("4df1e4b2c223f723", "dsv2_b32_ctx4096_fp8"): {"fetch_bytes": 89394731, "write_bytes": 37450015},
-    ("4df1e4b2c223f723", "llama2_7b_mla_b64_ctx8192_fp8"): {"fetch_bytes": 340412813, "write_bytes": 17065448},
+    ("907322d916f47c93", "dsv2_b32_ctx4096"): {"fetch_bytes": 155938064, "write_bytes": 16842752},
+    ("907322d916f47c93", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210597589, "write_bytes": 35258368},
+    ("907322d916f47c93", "dsv2_ragged_paged_256"): {"fetch_bytes": 4921561970, "write_bytes": 124741632},
 }
 
 
-ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip")
+ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip", "splitkv_r128.hip")
 
 
 EXTEND_SOURCES = ("attn_tile.hpp", "extend.hip")
@@ -91,6 +89,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer copies (0 = enough for >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mall-warm", action="store_true",
+                    help="also time steps that all reuse cache copy 0 (last-level cache may hold it)")
+    ap.add_argument("--attention-rows", type=int, default=0, choices=(0, 64, 128),
+                    help="split-KV rows per workgroup (0 = the library's choice by shape)")
     ap.add_argument("--separate", action="store_true",
                     help="decode workloads: time mla_append_latent + mla_decode instead of mla_decode_step")
     ap.add_argument("--path", choices=("auto", "absorbed", "expanded"), default="auto",
@@ -104,7 +106,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
+def build_state(wl, kv_chunk, rotate, path="auto", form="auto", attention_rows=0):
     import numpy as np
     import torch
 
@@ -184,6 +186,9 @@ def build_state(wl, kv_chunk, rotate, path="auto", form="auto"):
     for _ in range(R - 1):
         layers.append(mla.mla_fold_weights(cfg, w_dkv, w_uk, w_uv))
         caches.append(cache0.clone())
+    if attention_rows:
+        for layer in layers:
+            mla.mla_layer_set_attention_rows(layer, attention_rows)
     out_form = q_form = None
     if wl.kind == "hidden":
         q_form = {"auto": mla.mla_query_choose_form(cfg, int(wl.q_lens().sum())),
@@ -422,7 +427,7 @@ def main():
     wl = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     log(f"workload {wl.name}: {wl.description}")
-    st = build_state(wl, args.kv_chunk, args.rotate, args.path, args.form)
+    st = build_state(wl, args.kv_chunk, args.rotate, args.path, args.form, args.attention_rows)
     st["separate"] = args.separate
     if st["extend"] or st["project"]:
         return main_extend(args, wl, st)
@@ -492,23 +497,27 @@ def main():
     def pct(v, q):
         return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))] if v else None
 
-    # The same steps with every step on copy 0: the 256 MB last-level cache
-    # may then serve part of the cache from the previous step ("MALL-warm").
-    with torch.cuda.stream(cap):
-        g_warm = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_warm, stream=cap):
-            for r in range(R):
-                run_step(st, 0)
-    torch.cuda.current_stream().wait_stream(cap)
-    g_warm.replay()
-    torch.cuda.synchronize()
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record()
-    for i in range(max(1, K // R)):
+    # With --mall-warm, the same steps with every step on copy 0: the 256 MB
+    # last-level cache may then serve part of the cache from the previous
+    # step.  Off by default, so that every kernel launch of a default run
+    # (and of a profiler run of it) streams its cache copy from HBM.
+    warm_ms_step = None
+    if args.mall_warm:
+        with torch.cuda.stream(cap):
+            g_warm = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_warm, stream=cap):
+                for r in range(R):
+                    run_step(st, 0)
+        torch.cuda.current_stream().wait_stream(cap)
         g_warm.replay()
-    w1.record()
-    torch.cuda.synchronize()
-    warm_ms_step = w0.elapsed_time(w1) / (max(1, K // R) * R)
+        torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for i in range(max(1, K // R)):
+            g_warm.replay()
+        w1.record()
+        torch.cuda.synchronize()
+        warm_ms_step = w0.elapsed_time(w1) / (max(1, K // R) * R)
     # The attention kernel and the combine + output kernels on their own:
     # back-to-back launches in a graph, each on its own cache copy.
     mla = st["mla"]
@@ -543,6 +552,7 @@ def main():
             "workload": wl.name, "batch": wl.batch, "query_tokens": st["Tq"],
             "max_context": st["max_seq_len"], "heads": s.H, "kv_lora_rank": s.d_c,
             "qk_rope_head_dim": s.d_rope, "kv_chunk": st["chunk"], "rotated_copies": st["R"],
+            "attention_rows": args.attention_rows or "by shape",
         },
         "latent_cache_GBps": achieved,
         "latent_cache_frac_of_hbm_peak": achieved / HBM_PEAK_GBPS,

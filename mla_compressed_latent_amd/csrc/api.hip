@@ -131,12 +131,17 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
     // more than 32 rows: 64-row workgroups of eight waves, or (bf16 pages,
     // more than 64 rows) 128-row workgroups of four waves.  The 128-row
     // kernel's loop is the faster one per row, but its start (query rows and
-    // first tiles) and its write-out are longer and it takes twice the splits
-    // of the 64-row kernel: by shape it is taken for splits of 1024 tokens or
-    // more (measured, DeepSeek-V2 shape: 512-token splits at B32 x 4096, 60
-    // vs 52 us; 4096-token splits at B8 x 128k, 345 vs 375 us).
+    // first tiles) and its write-out are longer, it takes twice the splits
+    // of the 64-row kernel, and its long workgroups balance worse when there
+    // are more of them than compute units: by shape it is taken for splits
+    // of 1024 tokens or more when the batch's 128-row groups number at most
+    // one per compute unit (measured, DeepSeek-V2 shape: B32 x 4096, 512-token
+    // splits, 60 vs 52 us; B8 x 128k, 4096-token splits, 345 vs 375 us;
+    // 256 ragged sequences of up to 32k with one or two queries, 8192-token
+    // splits, 3.35 vs 2.47 ms).
     const bool r128_ok = rows > 64 && L->cfg.cache_format == MLA_CACHE_DTYPE;
-    bool use128 = r128_ok && chunk_for((rows + 127) / 128) >= 1024;
+    const int rq128 = (rows + 127) / 128;
+    bool use128 = r128_ok && (int64_t)batch * rq128 <= L->num_cus && chunk_for(rq128) >= 1024;
     if (L->attn_rows == 128) use128 = r128_ok;
     if (L->attn_rows == 64) use128 = false;
     if (use128) {
@@ -163,7 +168,7 @@ DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan
   DecodeLayout d;
   d.off_abuf = 0;
   d.off_opart = align256(rows * D * L->elem);
-  const size_t part_elem = p.NB == 128 ? 2 : 4;   // the 128-row kernel writes bf16 partials
+  const size_t part_elem = p.NB >= 8 ? 2 : 4;   // the 64- and 128-row kernels write bf16 partials
   d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * part_elem);
   d.off_olat = d.off_lse + align256((size_t)p.S_max * rows * 4);
   d.total = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
@@ -266,7 +271,7 @@ void decode_launch(const mla_layer* L, const void* q, const int32_t* cu_q, const
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
                         c.cache_format == MLA_CACHE_FP8, st);
   if (phases & MLA_PHASE_OUTPUT) {
-    const bool part_bf16 = p.NB == 128;   // the 128-row kernel writes bf16 partials
+    const bool part_bf16 = p.NB >= 8;   // the 64- and 128-row kernels write bf16 partials
     if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
       mla::launch_combine_out(p, opart, part_bf16, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
                               c.v_head_dim, L->num_cus, st);
@@ -859,7 +864,7 @@ mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* 
     mla::SplitPlan p;
     make_plan(L, batch, max_q_len, max_seq_len, 0, &p);
     const DecodeLayout d = decode_layout(L, total_q, p);
-    mla::launch_combine(L->elem, p, ws + d.off_opart, p.NB == 128, (const float*)(ws + d.off_lse), cu_q,
+    mla::launch_combine(L->elem, p, ws + d.off_opart, p.NB >= 8, (const float*)(ws + d.off_lse), cu_q,
                         seq_lens, batch, total_q, c.num_attention_heads, c.kv_lora_rank, ws + d.off_olat, st);
     act = ws + d.off_olat;
   }

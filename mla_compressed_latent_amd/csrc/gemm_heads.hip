@@ -43,7 +43,10 @@ __device__ __forceinline__ void store_bf16x4(bf16* dst, float a, float b, float 
 // blocks of 32 latent columns, up to kAbsorbTokBlocks token blocks): its
 // weight fragments stay in registers while the token blocks stream past, so
 // W_uk is read about once per step however many query tokens there are.
-// Each lane stores 4 consecutive latent values of one token.  The stored score
+// The 32 x JB*32 output block goes through LDS so that it leaves as whole
+// JB*64-byte row segments (16-byte stores, JB*4 lanes per row) instead of
+// 8-byte pieces of 32 rows per store (measured on the DeepSeek-V2 shape,
+// 32 tokens: 7.2 -> 5.1 us for the W_uk stream).  The stored score
 // operand (q_lat and the rotated rope part) is pre-multiplied by qscale =
 // softmax scale * log2(e), so the attention kernel's scores come out in log2
 // units.
@@ -96,6 +99,7 @@ __device__ __forceinline__ void absorb_block(
   const int jg = id % JG, h = (id / JG) % H, tbg = id / (JG * H);
   const int dq = dn + dr, D = dc + dr;
   const bf16* wh = wuk + (int64_t)h * dc * dn;
+  __shared__ __attribute__((aligned(16))) bf16 ost[32][JB * 32 + 8];
   bf16x8 wa[JB][NS];
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb)
@@ -108,20 +112,28 @@ __device__ __forceinline__ void absorb_block(
     for (int s = 0; s < NS; ++s) dst[s] = load_bf16x8(qrow + 16 * s);
   };
   auto compute = [&](int tb, const bf16x8 (&bq)[NS]) {
-    const int t = tb * 32 + l32;
+    // acc[4 r4 + e] is latent column jb*32 + 8 r4 + 4 g + e of token row l32
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       f32x16 acc = zero_f32x16();
 #pragma unroll
       for (int s = 0; s < NS; ++s) acc = mfma32(wa[jb][s], bq[s], acc);
-      if (t < Tq) {
-        bf16* dst = abuf + ((int64_t)t * H + h) * D + (jg * JB + jb) * 32 + 4 * g;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          store_bf16x4(dst + 8 * r4, acc[4 * r4] * qscale, acc[4 * r4 + 1] * qscale,
-                       acc[4 * r4 + 2] * qscale, acc[4 * r4 + 3] * qscale);
-      }
+      for (int r4 = 0; r4 < 4; ++r4)
+        store_bf16x4(&ost[l32][jb * 32 + 8 * r4 + 4 * g], acc[4 * r4] * qscale, acc[4 * r4 + 1] * qscale,
+                     acc[4 * r4 + 2] * qscale, acc[4 * r4 + 3] * qscale);
     }
+    __syncthreads();
+    constexpr int kLanesPerRow = JB * 4, kRowsPerStore = 64 / kLanesPerRow;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += kRowsPerStore) {
+      const int r = r0 + lane / kLanesPerRow, c = (lane % kLanesPerRow) * 8;
+      const int t = tb * 32 + r;
+      if (t < Tq)
+        *reinterpret_cast<bf16x8*>(abuf + ((int64_t)t * H + h) * D + jg * JB * 32 + c) =
+            *reinterpret_cast<const bf16x8*>(&ost[r][c]);
+    }
+    __syncthreads();   // the next token block reuses ost
   };
   // ping-pong over two statically indexed query buffers
   bf16x8 qa[NS], qb[NS];

@@ -93,19 +93,21 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
 // out[t][h][:] = (LSE-weighted merge of the split partials) . W_uv_h, one
 // workgroup per (32 query tokens, head); bf16 layers, at most kCombineMaxSplits.
 constexpr int kCombineMaxSplits = 64;
-// part_bf16: the partials are bf16 (the 128-row kernel's), else fp32.
+// part_bf16: the partials are bf16 (the 64- and 128-row kernels'), else fp32.
 void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
                         const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
                         int batch, int Tq, int H, int dv, int num_cus, hipStream_t st);
-// 64 query rows per workgroup, eight waves (bf16 layers, plan.NB == 8).
+// 64 query rows per workgroup, eight waves (bf16 layers, plan.NB == 8);
+// bf16 partials.
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                       int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                       int max_pages, int batch, int Tq, int H, int page_size, void* opart,
                        float* lse, bool fp8, hipStream_t st);
-// 128 query rows per workgroup, four waves (bf16 layers with bf16 pages, plan.NB == 128).
+// 128 query rows per workgroup, four waves (bf16 layers with bf16 pages,
+// plan.NB == 128); bf16 partials.
 void launch_splitkv_r128(const SplitPlan& plan, const void* abuf, const void* cache,
                          const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                         int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                         int max_pages, int batch, int Tq, int H, int page_size, void* opart,
                          float* lse, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,

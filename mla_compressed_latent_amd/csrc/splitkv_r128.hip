@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
     const bf16* __restrict__ abuf, const bf16* __restrict__ cache, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
-    float* __restrict__ opart, float* __restrict__ lse) {
+    bf16* __restrict__ opart, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kRBuf][kTileTok * kD];
   // swap slot of wave w: first w's partial scores of row block w ^ 1 (16
   // registers x 64 lanes, fp32), then row block w ^ 1's probabilities
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
                                    (128 * wave + 32 * cb + 8 * q4 + 4 * g) * 2) = v;
       }
   __syncthreads();
-  bf16* const part = reinterpret_cast<bf16*>(opart);
+  bf16* const part = opart;
   for (int r = wave; r < kRRows; r += 4) {
     const int row = row_base + r;
     if (row >= R) break;
@@ -575,12 +575,12 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
 
 void launch_splitkv_r128(const SplitPlan& plan, const void* abuf, const void* cache,
                          const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                         int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                         int max_pages, int batch, int Tq, int H, int page_size, void* opart,
                          float* lse, hipStream_t st) {
   const int nblocks = batch * plan.S_max * plan.RQ;
   splitkv_bf16_r128_kernel<<<nblocks, 256, 0, st>>>(
       (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
+      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse);
 }
 
 }  // namespace mla

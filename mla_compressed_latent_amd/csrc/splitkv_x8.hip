@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
     const bf16* __restrict__ abuf, const void* __restrict__ cache_v, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
-    float* __restrict__ opart, float* __restrict__ lse) {
+    bf16* __restrict__ opart, float* __restrict__ lse) {
   constexpr int kBuf = F8 ? 3 : kX8Buf;
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kBuf][kTileTok * kD];
   __shared__ __attribute__((aligned(1024))) char stage[F8 ? 2 : 1][F8 ? kF8StageBytes : 16];
@@ -383,15 +383,16 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       const float l = lrow_s[32 * rb + l32];
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int64_t rowg = (int64_t)(q0 + row / H) * H + row % H;
-      float* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + 128 * v;
+      bf16* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + 128 * v;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 o;
+          bf16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = O[db][rb][4 * q4 + e] * inv;
-          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q4 + 4 * g) = o;
+          for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(O[db][rb][4 * q4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * q4 + 4 * g) = o;
         }
     }
   }
@@ -401,17 +402,17 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
 
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
-                       int max_pages, int batch, int Tq, int H, int page_size, float* opart,
+                       int max_pages, int batch, int Tq, int H, int page_size, void* opart,
                        float* lse, bool fp8, hipStream_t st) {
   const int nblocks = batch * plan.S_max * plan.RQ;
   if (fp8)
     splitkv_bf16_x8_kernel<true><<<nblocks, 512, 0, st>>>(
         (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-        plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
+        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse);
   else
     splitkv_bf16_x8_kernel<false><<<nblocks, 512, 0, st>>>(
         (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-        plan.chunk, plan.S_max, plan.RQ, Tq, opart, lse);
+        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse);
 }
 
 }  // namespace mla

@@ -76,7 +76,7 @@ def test_no_alloc_fp32_layer_two_calls():
 
 def test_no_alloc_rejects_a_workspace_beyond_the_scratch():
     mla = __import__("mla_compressed_latent_amd")
-    wl = workload("dsv2_b32_ctx4096", name="noalloc_over", shape=SMALL_DSV2, batch=4, fixed_prefix=4500)
+    wl = workload("dsv2_b32_ctx4096", name="noalloc_over", shape=SMALL_DSV2, batch=8, fixed_prefix=4500)
     case = _case(wl, 64)
     need = mla.mla_decode_workspace_bytes(case.layer, wl.batch, case.q.shape[0], case.max_q_len,
                                           case.max_seq_len, 64)
