@@ -262,6 +262,25 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 constexpr int kCombThreads = 512;
 constexpr int kCombRowPad = 8;   // bf16 pad per LDS row of o_lat
 
+// E consecutive elements of a split partial row, loaded as one vector (16
+// bytes, or 8 for bf16 partials in blocks of 4 tokens) and read as floats.
+template <typename P, int E> struct PartVec;
+template <> struct PartVec<float, 4> {
+  typedef f32x4 T;
+  static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ float get(const T& v, int e) { return v[e]; }
+};
+template <> struct PartVec<bf16, 4> {
+  typedef __bf16 T __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ T load(const bf16* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ float get(const T& v, int e) { return static_cast<float>(v[e]); }
+};
+template <> struct PartVec<bf16, 8> {
+  typedef bf16x8 T;
+  static __device__ __forceinline__ T load(const bf16* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ float get(const T& v, int e) { return static_cast<float>(v[e]); }
+};
+
 template <int TB, typename P>
 __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
     const P* __restrict__ opart, const float* __restrict__ lse, const int32_t* __restrict__ cu_q,
@@ -276,7 +295,6 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 ob[32][kDc + kCombRowPad];
   constexpr int kGrp = 8;
   __shared__ __attribute__((aligned(1024))) bf16 wsec[4][2 * kGrp * 512];   // 16 fragments per wave
-  const int32_t* cu = stage_cu(cu_st, cu_q, batch);
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H, tb = blockIdx.x / H;
   const int64_t rows_total = (int64_t)Tq * H;
@@ -302,6 +320,48 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       dma16(wh + ((int64_t)wsel * (kDc / 16) + 2 * kGrp + u) * 64 * 8, (uint32_t)lane * 16u, dst + u * 1024);
   }
 
+  // This thread's partial rows and the block's log2-sum-exps: the first
+  // round of partial loads and all lse loads are issued before the number of
+  // splits each row's sequence has is known (the workspace holds S_max splits
+  // of every row, so the loads stay in bounds; splits past a sequence's end
+  // hold stale values that the weights below mask), so their latency runs
+  // under the token -> sequence lookups.
+  // Each thread takes kE consecutive elements (16 bytes of partial) of rows
+  // r0, r0 + kGroups, ...
+  constexpr int kE = (sizeof(P) == 2 && TB >= 8) ? 8 : 4;
+  constexpr int kThrRow = kDc / kE;                    // threads per row
+  constexpr int kGroups = kCombThreads / kThrRow;      // rows in flight at once
+  constexpr int kRows = TB / kGroups;                  // rows per thread
+  constexpr int kSp = 16 / kRows;                      // splits per round of loads
+  typedef PartVec<P, kE> PV;
+  const int j = kE * (tid % kThrRow), r0 = tid / kThrRow;
+  float oacc[kRows][kE];
+  const P* src[kRows];
+#pragma unroll
+  for (int u = 0; u < kRows; ++u) {
+#pragma unroll
+    for (int e = 0; e < kE; ++e) oacc[u][e] = 0.f;
+    const int t = min(tb * TB + r0 + kGroups * u, Tq - 1);   // rows past Tq read a valid row, weight 0
+    src[u] = opart + ((int64_t)t * H + h) * kDc + j;
+  }
+  typename PV::T v[kSp][kRows];
+#pragma unroll
+  for (int d = 0; d < kSp; ++d)
+#pragma unroll
+    for (int u = 0; u < kRows; ++u)
+      if (d < S_max) v[d][u] = PV::load(src[u] + d * rows_total * kDc);
+
+  constexpr int kLseTot = kCombineMaxSplits * TB;   // (split, row) pairs
+  constexpr int kLsePerThread = (kLseTot + kCombThreads - 1) / kCombThreads;
+  float x[kLsePerThread];
+#pragma unroll
+  for (int u = 0; u < kLsePerThread; ++u) {
+    const int k = tid + kCombThreads * u, sp = k / TB, r = k % TB;
+    const int t = min(tb * TB + r, Tq - 1);
+    x[u] = (k < kLseTot && sp < S_max) ? lse[sp * rows_total + (int64_t)t * H + h] : -INFINITY;
+  }
+
+  const int32_t* cu = stage_cu(cu_st, cu_q, batch);
   if (tid < TB) {
     const int t = tb * TB + tid;
     int sb = 0;
@@ -309,56 +369,26 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
     sb_s[tid] = sb;
   }
   __syncthreads();
-
-  // This thread's partial rows: the first round of their loads is issued
-  // before the split weights are known, so its latency runs under the lse
-  // loads and the weight computation.
-  constexpr int kRows = TB * (kDc / 4) / kCombThreads;   // rows per thread (TB / 4)
-  constexpr int kSp = 16 / kRows;                        // splits per round of loads
-  const int j = 4 * (tid & 127), r0 = tid >> 7;
-  f32x4 oacc[kRows];
-  const P* src[kRows];
-#pragma unroll
-  for (int u = 0; u < kRows; ++u) {
-    oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int t = min(tb * TB + r0 + 4 * u, Tq - 1);   // rows past Tq read a valid row, weight 0
-    src[u] = opart + ((int64_t)t * H + h) * kDc + j;
-  }
   // splits a row's sequence has (the rows of one thread are the same for
   // the whole wave, so these guards never diverge)
   int sb[kRows], smax = 0;
 #pragma unroll
   for (int u = 0; u < kRows; ++u) {
-    sb[u] = sb_s[r0 + 4 * u];
+    sb[u] = sb_s[r0 + kGroups * u];
     smax = max(smax, sb[u]);
   }
-  f32x4 v[kSp][kRows];
   auto load_round = [&](int sp0) {
 #pragma unroll
     for (int d = 0; d < kSp; ++d)
 #pragma unroll
       for (int u = 0; u < kRows; ++u)
         if (sp0 + d < sb[u])
-          v[d][u] = load4_f32(src[u] + (sp0 + d) * rows_total * kDc);
+          v[d][u] = PV::load(src[u] + (sp0 + d) * rows_total * kDc);
   };
-  load_round(0);
-
-  constexpr int kLseTot = kCombineMaxSplits * TB;   // (split, row) pairs
-  constexpr int kLsePerThread = (kLseTot + kCombThreads - 1) / kCombThreads;
-  {
-    float x[kLsePerThread];
 #pragma unroll
-    for (int u = 0; u < kLsePerThread; ++u) {
-      const int k = tid + kCombThreads * u, sp = k / TB, r = k % TB;
-      x[u] = (k < kLseTot && sp < S_max && sp < sb_s[r])
-                 ? lse[sp * rows_total + (int64_t)(tb * TB + r) * H + h]
-                 : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < kLsePerThread; ++u) {
-      const int k = tid + kCombThreads * u;
-      if (k < kLseTot && k / TB < S_max) w_s[k / TB][k % TB] = x[u];
-    }
+  for (int u = 0; u < kLsePerThread; ++u) {
+    const int k = tid + kCombThreads * u, sp = k / TB, r = k % TB;
+    if (k < kLseTot && sp < S_max) w_s[sp][r] = sp < sb_s[r] ? x[u] : -INFINITY;
   }
   __syncthreads();
   if (tid < TB) {
@@ -382,18 +412,24 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       for (int d = 0; d < kSp; ++d)
 #pragma unroll
         for (int u = 0; u < kRows; ++u) {
-          const float w = (sp0 + d < sb[u]) ? w_s[sp0 + d][r0 + 4 * u] : 0.f;
-          if (w != 0.f) oacc[u] += w * v[d][u];
+          const float w = (sp0 + d < sb[u]) ? w_s[sp0 + d][r0 + kGroups * u] : 0.f;
+          if (w != 0.f) {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) oacc[u][e] += w * PV::get(v[d][u], e);
+          }
         }
     }
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
-      const int r = r0 + 4 * u;
+      const int r = r0 + kGroups * u;
       const float inv = inv_s[r];
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 o = {from_f32<bf16>(oacc[u][0] * inv), from_f32<bf16>(oacc[u][1] * inv),
-                  from_f32<bf16>(oacc[u][2] * inv), from_f32<bf16>(oacc[u][3] * inv)};
-      *reinterpret_cast<bf16x4*>(&ob[r][j]) = o;
+#pragma unroll
+      for (int e = 0; e < kE; e += 4) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o = {from_f32<bf16>(oacc[u][e] * inv), from_f32<bf16>(oacc[u][e + 1] * inv),
+                    from_f32<bf16>(oacc[u][e + 2] * inv), from_f32<bf16>(oacc[u][e + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(&ob[r][j + e]) = o;
+      }
     }
   }
   if (copies_half) wait_vmcnt<0>();   // the copied half-block is in LDS
