@@ -24,6 +24,13 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 // float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
 
+// Two floats as a packed bf16 pair (round to nearest even), lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {from_f32<bf16>(lo), from_f32<bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Rotary angle for pair i at position pos, computed in double:
 // theta_i = base^(-2i/d_rope), angle = pos * theta_i.  Long positions
 // (1e5 and more) need the double product and double sin/cos.

@@ -384,15 +384,29 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int64_t rowg = (int64_t)(q0 + row / H) * H + row % H;
       bf16* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + 128 * v;
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      // lane half g holds columns 8 q4 + 4 g .. + 3; one swap of the lane
+      // halves per dword gives the lower half all of group q4 = 2p and the
+      // upper half all of group 2p + 1, written as 16 bytes per lane
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          bf16x4 o;
+        for (int p = 0; p < 2; ++p) {
+          uint32_t a[2], bq[2];   // groups 2p (a) and 2p + 1 (bq), this lane's 4 columns as 2 dwords
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(O[db][rb][4 * q4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * q4 + 4 * g) = o;
+          for (int k = 0; k < 2; ++k) {
+            a[k] = pack_bf16x2(O[db][rb][8 * p + 2 * k] * inv, O[db][rb][8 * p + 2 * k + 1] * inv);
+            bq[k] = pack_bf16x2(O[db][rb][8 * p + 4 + 2 * k] * inv, O[db][rb][8 * p + 4 + 2 * k + 1] * inv);
+          }
+          u32x4 w;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t send = g ? a[k] : bq[k];
+            const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            const uint32_t got = g ? r[0] : r[1];   // the other half's dword
+            w[k] = g ? got : a[k];
+            w[2 + k] = g ? bq[k] : got;
+          }
+          *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * p + 8 * g) = w;
         }
     }
   }
