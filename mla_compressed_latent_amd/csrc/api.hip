@@ -154,14 +154,19 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
   }
   p->chunk = chunk_for(p->RQ);
   p->S_max = (max_seq_len + p->chunk - 1) / p->chunk;
+  // More workgroups than compute units: launch from a device-built list of
+  // the items that have rows and tokens (ragged batches otherwise launch
+  // many that exit at once, interleaved with the busy ones).
+  p->list = (p->NB == 8 || p->NB == 128) && p->RQ <= 4096 &&
+            (int64_t)batch * p->S_max * p->RQ > L->num_cus;
   return p->S_max <= 1024;   // split weights of one row are staged on chip
 }
 
 struct DecodeLayout {
-  size_t off_abuf, off_opart, off_lse, off_olat, total;
+  size_t off_abuf, off_opart, off_lse, off_olat, off_work, total;
 };
 
-DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan& p) {
+DecodeLayout decode_layout(const mla_layer* L, int batch, int total_q, const mla::SplitPlan& p) {
   const mla_config& c = L->cfg;
   const size_t rows = (size_t)total_q * c.num_attention_heads;
   const size_t D = (size_t)c.kv_lora_rank + c.qk_rope_head_dim;
@@ -171,7 +176,8 @@ DecodeLayout decode_layout(const mla_layer* L, int total_q, const mla::SplitPlan
   const size_t part_elem = p.NB >= 8 ? 2 : 4;   // the 64- and 128-row kernels write bf16 partials
   d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * part_elem);
   d.off_olat = d.off_lse + align256((size_t)p.S_max * rows * 4);
-  d.total = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
+  d.off_work = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
+  d.total = d.off_work + (p.list ? align256(mla::work_list_bytes(batch, p)) : 0);
   return d;
 }
 
@@ -243,7 +249,7 @@ mla_status decode_prepare(const mla_layer* L, const void* q, const int32_t* cu_q
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: kv_chunk must be 0 or a multiple of 64 up to 8192");
   if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, p))
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: cannot plan the split");
-  *d = decode_layout(L, total_q, *p);
+  *d = decode_layout(L, batch, total_q, *p);
   if (workspace_bytes < d->total)
     return fail(MLA_ERR_INSUFFICIENT_WORKSPACE, "decode workspace holds %zu bytes, %zu needed",
                 workspace_bytes, d->total);
@@ -269,7 +275,7 @@ void decode_launch(const mla_layer* L, const void* q, const int32_t* cu_q, const
   if (phases & MLA_PHASE_ATTEND)
     mla::launch_splitkv(L->elem, p, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, total_q, H,
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
-                        c.cache_format == MLA_CACHE_FP8, st);
+                        c.cache_format == MLA_CACHE_FP8, ws + d.off_work, st);
   if (phases & MLA_PHASE_OUTPUT) {
     const bool part_bf16 = p.NB >= 8;   // the 64- and 128-row kernels write bf16 partials
     if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
@@ -548,7 +554,7 @@ size_t mla_decode_workspace_bytes(const mla_layer* L, int32_t batch, int32_t tot
     return 0;
   mla::SplitPlan p;
   if (!make_plan(L, batch, max_q_len, max_seq_len, kv_chunk, &p)) return 0;
-  return decode_layout(L, total_q, p).total;
+  return decode_layout(L, batch, total_q, p).total;
 }
 
 mla_status mla_decode_phases(const mla_layer* L, const void* q, const int32_t* cu_q,
@@ -863,7 +869,7 @@ mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* 
     if (s != MLA_OK) return s;
     mla::SplitPlan p;
     make_plan(L, batch, max_q_len, max_seq_len, 0, &p);
-    const DecodeLayout d = decode_layout(L, total_q, p);
+    const DecodeLayout d = decode_layout(L, batch, total_q, p);
     mla::launch_combine(L->elem, p, ws + d.off_opart, p.NB >= 8, (const float*)(ws + d.off_lse), cu_q,
                         seq_lens, batch, total_q, c.num_attention_heads, c.kv_lora_rank, ws + d.off_olat, st);
     act = ws + d.off_olat;

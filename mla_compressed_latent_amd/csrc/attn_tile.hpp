@@ -29,6 +29,32 @@ __device__ __forceinline__ int swz(int t) { return ((t >> 1) ^ (t >> 4)) & 7; }
 
 typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 
+// The (sequence b, split s, row group rq) a split-KV workgroup takes.  Without
+// a work list: the block's logical id in the full grid of batch x S_max x RQ
+// blocks (row group fastest), some of which find no rows or no tokens and
+// exit.  With one (built by the work-list kernel: only busy items, in the
+// same order, item.y = s << 12 | rq): blocks past *n_items exit at once.
+// Consecutive logical ids run on one XCD either way, so the row groups of a
+// split share its L2.
+__device__ __forceinline__ bool split_work_item(const int2* __restrict__ items, const int* __restrict__ n_items,
+                                                int batch, int S_max, int RQ, int* b, int* s, int* rq) {
+  if (items) {
+    const int n = __builtin_amdgcn_readfirstlane(*n_items);
+    if ((int)blockIdx.x >= n) return false;
+    const int2 it = items[xcd_logical_block(blockIdx.x, n)];
+    *b = __builtin_amdgcn_readfirstlane(it.x);
+    const int y = __builtin_amdgcn_readfirstlane(it.y);
+    *s = y >> 12;
+    *rq = y & 4095;
+    return true;
+  }
+  const int logical = xcd_logical_block(blockIdx.x, batch * S_max * RQ);
+  *rq = logical % RQ;
+  *s = (logical / RQ) % S_max;
+  *b = logical / (RQ * S_max);
+  return true;
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // (i mod 4) of the 8-byte words addressed by lanes 4j + i/4, j = 0..3.
 __device__ __forceinline__ v4bf16 ds_read_tr16(const char* p) {

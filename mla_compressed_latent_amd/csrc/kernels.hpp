@@ -84,12 +84,17 @@ struct SplitPlan {
   int RQ;       // row groups per sequence (bf16 path)
   int NB;       // bf16 path: 1 = one 32-row block per workgroup, 8 = 64-row eight-wave kernel,
                 // 128 = 128-row four-wave kernel (bf16 pages)
+  bool list;    // NB 8 / 128: launch from a device-built list of busy work items
 };
+// Work-list size (bytes) for a plan: an int2 per possible item and the count.
+inline size_t work_list_bytes(int batch, const SplitPlan& p) {
+  return ((size_t)batch * p.S_max * p.RQ + 1) * 8;
+}
 // fp8: the cache holds MLA_CACHE_FP8 pages (bf16 layers).
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
-                    float scale, float* opart, float* lse, bool fp8, hipStream_t st);
+                    float scale, float* opart, float* lse, bool fp8, void* work, hipStream_t st);
 // out[t][h][:] = (LSE-weighted merge of the split partials) . W_uv_h, one
 // workgroup per (32 query tokens, head); bf16 layers, at most kCombineMaxSplits.
 constexpr int kCombineMaxSplits = 64;
@@ -102,13 +107,13 @@ void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                       float* lse, bool fp8, hipStream_t st);
+                       float* lse, bool fp8, const int2* items, const int* n_items, hipStream_t st);
 // 128 query rows per workgroup, four waves (bf16 layers with bf16 pages,
 // plan.NB == 128); bf16 partials.
 void launch_splitkv_r128(const SplitPlan& plan, const void* abuf, const void* cache,
                          const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                          int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                         float* lse, hipStream_t st);
+                         float* lse, const int2* items, const int* n_items, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

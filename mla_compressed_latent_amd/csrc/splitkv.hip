@@ -523,22 +523,73 @@ __global__ __launch_bounds__(128) void combine_kernel(const P* __restrict__ opar
 
 }  // namespace
 
+namespace {
+
+constexpr int kListThreads = 1024;
+
+// Busy work items of a split-KV launch, in the order of the full grid
+// (sequence, then split, then row group): sequence b contributes
+// min(RQ, ceil(rows_b / rows)) row groups x min(S_max, ceil(L_b / chunk))
+// splits.  One workgroup: each thread counts a contiguous range of
+// sequences, a block-wide scan gives the ranges' offsets, each thread writes
+// its items; the last thread writes the count.
+__global__ __launch_bounds__(kListThreads) void work_list_kernel(const int32_t* __restrict__ cu_q,
+                                                                 const int32_t* __restrict__ seq_lens, int batch,
+                                                                 int H, int rows, int chunk, int S_max, int RQ,
+                                                                 int2* __restrict__ items, int* __restrict__ n_items) {
+  __shared__ int tot[kListThreads];
+  const int tid = threadIdx.x;
+  const int per = (batch + kListThreads - 1) / kListThreads;
+  const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
+  auto groups = [&](int b) { return min(RQ, ((cu_q[b + 1] - cu_q[b]) * H + rows - 1) / rows); };
+  auto splits = [&](int b) { return min(S_max, (seq_lens[b] + chunk - 1) / chunk); };
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += max(0, groups(b)) * max(0, splits(b));
+  tot[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kListThreads; off <<= 1) {
+    const int v = tid >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  int pos = tot[tid] - mine;
+  for (int b = b0; b < b1; ++b) {
+    const int ng = groups(b), ns = splits(b);
+    for (int sp = 0; sp < ns; ++sp)
+      for (int rq = 0; rq < ng; ++rq) items[pos++] = make_int2(b, (sp << 12) | rq);
+  }
+  if (tid == kListThreads - 1) n_items[0] = tot[tid];
+}
+
+}  // namespace
+
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
                     const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                     int max_pages, int batch, int Tq, int H, int dc, int dr, int page_size,
-                    float scale, float* opart, float* lse, bool fp8, hipStream_t st) {
+                    float scale, float* opart, float* lse, bool fp8, void* work, hipStream_t st) {
   // bf16 layers: the absorbed queries already carry scale * log2(e)
   const float scale_log2e = elem == 2 ? 1.f : scale * 1.4426950408889634f;
   if (elem == 2) {
     const int nblocks = batch * plan.S_max * plan.RQ;
+    const int2* items = nullptr;
+    const int* n_items = nullptr;
+    if (plan.list && (plan.NB == 8 || plan.NB == 128)) {
+      int* count = reinterpret_cast<int*>(work);
+      int2* list = reinterpret_cast<int2*>(count + 2);
+      work_list_kernel<<<1, kListThreads, 0, st>>>(cu_q, seq_lens, batch, H, plan.NB == 128 ? 128 : 64,
+                                                   plan.chunk, plan.S_max, plan.RQ, list, count);
+      items = list;
+      n_items = count;
+    }
     switch (plan.NB) {
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                          page_size, opart, lse, fp8, st);
+                          page_size, opart, lse, fp8, items, n_items, st);
         break;
       case 128:
         launch_splitkv_r128(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                            page_size, opart, lse, st);
+                            page_size, opart, lse, items, n_items, st);
         break;
       default:
         if (fp8)

@@ -97,6 +97,19 @@ def test_bf16_dsv2_ragged_paged_two_queries(rows):
     _check(case, out, tag=f"dsv2_ragged_small rows={rows}")
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+def test_work_list_ragged(rows):
+    """More workgroups than compute units on a ragged batch: the attention
+    launches from the device-built list of busy (sequence, split, row group)
+    items.  Sampled heads against the oracle."""
+    wl = workload("dsv2_ragged_paged_256", name=f"worklist_{rows}", shape=SMALL_DSV2, batch=40, max_prefix=400)
+    case, out = _run(wl, kv_chunk=64, rows=rows)
+    _check(case, out, heads=[0, 77, 127], tag=f"work list rows={rows}")
+    again = case.decode(kv_chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "work-list launch not deterministic"
+
+
 def test_attention_rows_override_is_validated():
     import mla_compressed_latent_amd as mla
     case = GpuCase(workload("dsv2_b32_ctx4096", name="rows_arg", shape=SMALL_DSV2, batch=1, fixed_prefix=16))
