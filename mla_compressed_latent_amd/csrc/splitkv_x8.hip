@@ -27,10 +27,12 @@
 // of the previous one.
 //
 // F8 (MLA_CACHE_FP8 pages): three bf16 tiles and two FP8 staging buffers; the
-// value waves copy each FP8 tile to staging one tile ahead and, besides their
-// value product for tile it-1, convert a quarter of tile it+1's latent codes
-// and its rope keys; the score waves convert the other three quarters after
-// their softmax (the value waves' chain is the longer one).  Score and value waves run separate loops with the same
+// value waves copy each FP8 tile to staging one tile ahead (and convert tile
+// 0 before the loop); the score waves convert all of tile it+1 -- four
+// latent items and one rope item per lane, its staging reads issued before
+// their score MFMAs of tile it and the conversions spread between them -- so
+// that the conversion runs under matrix work instead of on the value waves'
+// chain (measured there: 1.5-1.7k of a 3.5k-clock tile).  Score and value waves run separate loops with the same
 // barrier sequence, so their operands (query, O) can share the AGPR file.
 #include "attn_tile.hpp"
 #include "common.hpp"
@@ -131,6 +133,54 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
       if (it == ntiles) break;
       const char* tileb = reinterpret_cast<const char*>(&tiles[it % kBuf][0]);
+      // FP8: this lane's items of tile it+1 (its staging landed before the
+      // barrier): latent items 64 wave + lane + 256 u, u < 4 (row i / 32,
+      // codes 16 (i % 32) .. + 15 -> bf16 chunks 2 (i % 32), + 1) and rope
+      // item 64 wave + lane (row i / 8, chunk 64 + i % 8); rows past the
+      // tile's valid rows are written as zeros.  Their staging reads go out
+      // now, the conversions and writes between the score MFMAs below.
+      const u32x4 zero4 = {0u, 0u, 0u, 0u};
+      u32x4 cw[4], rw = zero4;
+      float cs[4];
+      int nv1 = 0;
+      char* ctile = reinterpret_cast<char*>(&tiles[(it + 1) % kBuf][0]);
+      const bool conv = F8 && it + 1 < ntiles;
+      if constexpr (F8) {
+        if (conv) {
+          const char* stg = &stage[(it + 1) & 1][0];
+          const float* scales = reinterpret_cast<const float*>(stg + kF8RowsBytes);
+          nv1 = tok_end - (tok_begin + (it + 1) * kTileTok);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 64 * wave + lane + 256 * u, t = i >> 5;
+            cw[u] = t < nv1 ? *reinterpret_cast<const u32x4*>(stg + t * kF8Row + (i & 31) * 16) : zero4;
+            cs[u] = t < nv1 ? scales[t] : 0.f;
+          }
+          const int i = 64 * wave + lane, t = i >> 3;
+          if (t < nv1) rw = *reinterpret_cast<const u32x4*>(stg + t * kF8Row + 512 + (i & 7) * 16);
+        }
+      }
+      auto put_latent = [&](int u) {
+        const int i = 64 * wave + lane + 256 * u, t = i >> 5, k = i & 31;
+        u32x4 lo = zero4, hi = zero4;
+        if (t < nv1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[u][q], cs[u], false));
+            const uint32_t y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[u][q], cs[u], true));
+            if (q < 2) {
+              lo[2 * q] = x;
+              lo[2 * q + 1] = y;
+            } else {
+              hi[2 * q - 4] = x;
+              hi[2 * q - 3] = y;
+            }
+          }
+        }
+        const int sw = swz(t);
+        *reinterpret_cast<u32x4*>(ctile + (t * kChunks + ((2 * k) ^ sw)) * 16) = lo;
+        *reinterpret_cast<u32x4*>(ctile + (t * kChunks + ((2 * k + 1) ^ sw)) * 16) = hi;
+      };
       f32x4 acc[2];
       {
         bf16x8 ring[kX8Ring][2];
@@ -149,6 +199,15 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
             for (int m = 0; m < 2; ++m)
               a[m] = *reinterpret_cast<const bf16x8*>(tileb + a_base[m][(st + kX8Ring) & 1] +
                                                       128 * ((st + kX8Ring) >> 1));
+          }
+          if constexpr (F8) {
+            if (conv) {
+              if (st == 2 || st == 6 || st == 10 || st == 14) put_latent((st - 2) / 4);
+              if (st == 16) {
+                const int i = 64 * wave + lane, t = i >> 3;
+                *reinterpret_cast<u32x4*>(ctile + (t * kChunks + 64 + ((i & 7) ^ swz(t))) * 16) = rw;
+              }
+            }
           }
         }
         qk16_drain(acc[0], acc[1]);
@@ -188,11 +247,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       l_run = l_run * alpha + rs;
       m_run = m_new;
       if (G == 0) alpha_s[it & 1][16 * wave + c16] = alpha;
-      if constexpr (F8)
-        if (it + 1 < ntiles)   // latent items 256..1023 of the next tile (value waves: the rest)
-          f8_convert<3>(&stage[(it + 1) & 1][0], reinterpret_cast<char*>(&tiles[(it + 1) % kBuf][0]),
-                        tok_end - (tok_begin + (it + 1) * kTileTok), 256 + 64 * wave + lane, 256,
-                        kTileTok * 32, 256);
     }
     if (G == 0) lrow_s[16 * wave + c16] = l_run;
     __syncthreads();   // row sums published
@@ -237,12 +291,11 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
         dma16(pg + (int64_t)page_size * kF8Row + (tok0 % page_size) * 4, (uint32_t)((lane & 7) * 16),
               dst + kF8RowsBytes);
     };
-    // tile 0 (prologue): all latent items; later tiles: items 0..255 and the
-    // rope items (the score waves convert 256..1023)
+    // tile 0, before the loop: all of its latent and rope items (the score
+    // waves convert every later tile)
     auto f8_convert_tile = [&](int it) {
       f8_convert<4>(&stage[it & 1][0], reinterpret_cast<char*>(&tiles[it % kBuf][0]),
-                    tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256,
-                    it == 0 ? kTileTok * 32 : 256, 0);
+                    tok_end - (tok_begin + it * kTileTok), 64 * v + lane, 256, kTileTok * 32, 0);
     };
     // value operand (transposing read, natural token order): in 16-lane group
     // G, source lane 4 j + q points at dims 4q..4q+3 of the group's 16 dims,
@@ -321,7 +374,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       __syncthreads();   // tile `it` landed; probabilities of tile it-1 published
       if constexpr (F8) {
         if (it + 2 < ntiles) f8_issue_part(it + 2);   // staging of tile it, converted already
-        if (it + 1 < ntiles) f8_convert_tile(it + 1);   // into tiles[(it - 2) % 3]
       } else {
         if (it + 2 < ntiles) issue_tile(it + 2);
       }
