@@ -22,6 +22,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("no GPU", allow_module_level=True)
 
 import mla_compressed_latent_amd as mla  # noqa: E402
+from oracle import mla_oracle  # noqa: E402
 from gpu_harness import SENTINEL_BYTE, GpuCase, errors, oracle_cache, oracle_outputs, oracle_query  # noqa: E402
 
 FP8_DSV2 = dataclasses.replace(DSV2, d_model=512, cache_format="fp8")
@@ -92,11 +93,23 @@ def test_append_fp8_rows():
             assert (pages[pg] == SENTINEL_BYTE).all()
 
 
+def _unquantized_outputs(case, b, heads):
+    """The oracle's attention over sequence b's rows WITHOUT the FP8 rounding
+    (information only: how far the quantized cache moves the output)."""
+    wl, s = case.wl, case.wl.shape
+    rows = oracle_cache(wl, b, case.w_dkv, quantize=False)
+    return mla_oracle.attend_sequence(wl.queries(b), rows, case.w_uk, case.w_uv, s.H, s.d_nope, s.d_v, s.rope_base,
+                                      mla_oracle.default_scale(s.d_nope, s.d_rope), heads)
+
+
 def _check(case, out, tag, heads=None):
+    """Parity against the oracle over its own quantized rows (asserted), and
+    the deviation from the unquantized oracle (printed beside it)."""
     wl = case.wl
     got = out.float().cpu().numpy()
     cu = wl.cu_q()
     worst = (0.0, 0.0)
+    dev = (0.0, 0.0)
     for b in range(wl.batch):
         ref = oracle_outputs(wl, b, heads, case.w_dkv, case.w_uk, case.w_uv)
         g = got[cu[b]:cu[b + 1]]
@@ -105,7 +118,10 @@ def _check(case, out, tag, heads=None):
         e = errors(g, ref)
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
         assert e[0] <= 1e-2 and e[1] <= 1e-2, f"{tag} seq {b}: {e}"
-    print(f"[fp8] {tag}: max|d|/max|ref| {worst[0]:.3e}, rms ratio {worst[1]:.3e}", flush=True)
+        u = errors(g, _unquantized_outputs(case, b, heads))
+        dev = (max(dev[0], u[0]), max(dev[1], u[1]))
+    print(f"[fp8] {tag}: max|d|/max|ref| {worst[0]:.3e}, rms ratio {worst[1]:.3e}; against the unquantized "
+          f"oracle (information): max|d|/max|ref| {dev[0]:.3e}, rms ratio {dev[1]:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("shape", [FP8_DSV2, FP8_LLAMA], ids=["128heads", "32heads"])

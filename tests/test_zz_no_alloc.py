@@ -64,6 +64,17 @@ def test_no_alloc_matches_decode_two_calls(rows):
         assert e[0] <= 1e-2 and e[1] <= 1e-2, (b, e)
 
 
+def test_no_alloc_with_work_list():
+    """A ragged batch big enough that the attention launches from its
+    device-built work list (kept in the scratch too)."""
+    wl = workload("dsv2_ragged_paged_256", name="noalloc_list", shape=SMALL_DSV2, batch=40, max_prefix=400)
+    case = _case(wl, 0)
+    # 128-token splits: 40 x 4 x 4 = 640 workgroups (more than one wave of
+    # them, so the list is used) in 31 MB of scratch
+    ref, got = _both(case, kv_chunk=128)
+    assert torch.equal(ref, got)
+
+
 def test_no_alloc_fp32_layer_two_calls():
     for batch, prefix in ((4, 250), (2, 90)):
         wl = WORKLOADS["tiny_f32"].with_(name=f"noalloc_f32_b{batch}", batch=batch, fixed_prefix=None,
