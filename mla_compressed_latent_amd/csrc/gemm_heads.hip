@@ -320,12 +320,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
       dma16(wh + ((int64_t)wsel * (kDc / 16) + 2 * kGrp + u) * 64 * 8, (uint32_t)lane * 16u, dst + u * 1024);
   }
 
-  // This thread's partial rows and the block's log2-sum-exps: the first
-  // round of partial loads and all lse loads are issued before the number of
-  // splits each row's sequence has is known (the workspace holds S_max splits
-  // of every row, so the loads stay in bounds; splits past a sequence's end
-  // hold stale values that the weights below mask), so their latency runs
-  // under the token -> sequence lookups.
+  // This thread's partial rows and the block's log2-sum-exps.  The lse loads
+  // are issued before the number of splits each row's sequence has is known
+  // (the workspace holds S_max splits of every row, so they stay in bounds;
+  // splits past a sequence's end hold stale values that the weights below
+  // mask); the partial rows are loaded only for splits the sequence has.
   // Each thread takes kE consecutive elements (16 bytes of partial) of rows
   // r0, r0 + kGroups, ...
   constexpr int kE = (sizeof(P) == 2 && TB >= 8) ? 8 : 4;
@@ -345,11 +344,6 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
     src[u] = opart + ((int64_t)t * H + h) * kDc + j;
   }
   typename PV::T v[kSp][kRows];
-#pragma unroll
-  for (int d = 0; d < kSp; ++d)
-#pragma unroll
-    for (int u = 0; u < kRows; ++u)
-      if (d < S_max) v[d][u] = PV::load(src[u] + d * rows_total * kDc);
 
   constexpr int kLseTot = kCombineMaxSplits * TB;   // (split, row) pairs
   constexpr int kLsePerThread = (kLseTot + kCombThreads - 1) / kCombThreads;
@@ -385,6 +379,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_out_bf16_kernel(
         if (sp0 + d < sb[u])
           v[d][u] = PV::load(src[u] + (sp0 + d) * rows_total * kDc);
   };
+  load_round(0);
 #pragma unroll
   for (int u = 0; u < kLsePerThread; ++u) {
     const int k = tid + kCombThreads * u, sp = k / TB, r = k % TB;
