@@ -32,16 +32,19 @@ typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 // The (sequence b, split s, row group rq) a split-KV workgroup takes.  Without
 // a work list: the block's logical id in the full grid of batch x S_max x RQ
 // blocks (row group fastest), some of which find no rows or no tokens and
-// exit.  With one (built by the work-list kernel: only busy items, in the
-// same order, item.y = s << 12 | rq): blocks past *n_items exit at once.
-// Consecutive logical ids run on one XCD either way, so the row groups of a
-// split share its L2.
-__device__ __forceinline__ bool split_work_item(const int2* __restrict__ items, const int* __restrict__ n_items,
+// exit; consecutive logical ids run on one XCD, so the row groups of a split
+// share its L2.  With one (built by the work-list kernel: only busy items,
+// item.y = s << 12 | rq, each XCD's items contiguous with a split's row
+// groups together): blocks are handed to the 8 XCDs in turn, so block id % 8
+// names the XCD and id / 8 the item among its list_hdr[1 + x] items, which
+// start at list_hdr[9 + x]; blocks past that count exit at once.
+__device__ __forceinline__ bool split_work_item(const int2* __restrict__ items, const int* __restrict__ list_hdr,
                                                 int batch, int S_max, int RQ, int* b, int* s, int* rq) {
   if (items) {
-    const int n = __builtin_amdgcn_readfirstlane(*n_items);
-    if ((int)blockIdx.x >= n) return false;
-    const int2 it = items[xcd_logical_block(blockIdx.x, n)];
+    const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int n = __builtin_amdgcn_readfirstlane(list_hdr[1 + x]);
+    if (local >= n) return false;
+    const int2 it = items[__builtin_amdgcn_readfirstlane(list_hdr[9 + x]) + local];
     *b = __builtin_amdgcn_readfirstlane(it.x);
     const int y = __builtin_amdgcn_readfirstlane(it.y);
     *s = y >> 12;

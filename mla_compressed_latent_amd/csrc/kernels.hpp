@@ -86,9 +86,19 @@ struct SplitPlan {
                 // 128 = 128-row four-wave kernel (bf16 pages)
   bool list;    // NB 8 / 128: launch from a device-built list of busy work items
 };
-// Work-list size (bytes) for a plan: an int2 per possible item and the count.
+// Work list of a plan (bytes at its work pointer): a header of
+// kListHeaderInts ints ([0] busy items, [1 + x] items of XCD x, [9 + x] where
+// they start), the items (an int2 per possible item), then scratch for the
+// ranked splits (an int2 per possible split).
+constexpr int kListHeaderInts = 32;
 inline size_t work_list_bytes(int batch, const SplitPlan& p) {
-  return ((size_t)batch * p.S_max * p.RQ + 1) * 8;
+  return kListHeaderInts * 4 + ((size_t)batch * p.S_max * p.RQ + (size_t)batch * p.S_max) * 8;
+}
+// Workgroups of a launch from the work list: block id % 8 picks an XCD's
+// items, id / 8 the item.  An XCD holds at most 2 ceil(batch S_max / 16)
+// splits of at most RQ row groups each.
+inline int work_list_grid(int batch, const SplitPlan& p) {
+  return 8 * p.RQ * 2 * ((batch * p.S_max + 15) / 16);
 }
 // fp8: the cache holds MLA_CACHE_FP8 pages (bf16 layers).
 void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const void* cache,
@@ -107,13 +117,13 @@ void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                       float* lse, bool fp8, const int2* items, const int* n_items, hipStream_t st);
+                       float* lse, bool fp8, const int2* items, const int* list_hdr, hipStream_t st);
 // 128 query rows per workgroup, four waves (bf16 layers with bf16 pages,
 // plan.NB == 128); bf16 partials.
 void launch_splitkv_r128(const SplitPlan& plan, const void* abuf, const void* cache,
                          const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                          int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                         float* lse, const int2* items, const int* n_items, hipStream_t st);
+                         float* lse, const int2* items, const int* list_hdr, hipStream_t st);
 // olat[t][h][:] = LSE-weighted merge of the split partials
 void launch_combine(int elem, const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
                     const int32_t* cu_q, const int32_t* seq_lens, int batch, int Tq, int H, int dc,

@@ -526,40 +526,107 @@ __global__ __launch_bounds__(128) void combine_kernel(const P* __restrict__ opar
 namespace {
 
 constexpr int kListThreads = 1024;
+constexpr int kListBins = kMaxChunkTokens / 32 + 1;   // tile counts of a split: 1 .. chunk / 32
+static_assert(kListBins <= kListThreads, "one thread per tile count in the rank scan");
 
-// Busy work items of a split-KV launch, in the order of the full grid
-// (sequence, then split, then row group): sequence b contributes
-// min(RQ, ceil(rows_b / rows)) row groups x min(S_max, ceil(L_b / chunk))
-// splits.  One workgroup: each thread counts a contiguous range of
-// sequences, a block-wide scan gives the ranges' offsets, each thread writes
-// its items; the last thread writes the count.
+// Busy work items of a split-KV launch, balanced over the 8 XCDs.  A split
+// (b, s) of sequence b brings min(RQ, ceil(rows_b / rows)) row groups, which
+// stay together on one XCD (they read the same tiles through its L2).  The
+// splits are ranked by tile count, largest first (counting sort), and dealt
+// to the XCDs in a snake (ranks 16 k + x and 16 k + 15 - x go to XCD x), so
+// every XCD gets a similar mix of long and short splits and starts its long
+// ones first.  Header: [0] busy items, [1 + x] items of XCD x, [9 + x] where
+// they start; grp (batch x S_max entries) holds the ranked splits.  One
+// workgroup: ranks come from atomic counters in LDS, so equal-size splits
+// take an arbitrary order among themselves (each item's results do not
+// depend on where it runs).
 __global__ __launch_bounds__(kListThreads) void work_list_kernel(const int32_t* __restrict__ cu_q,
                                                                  const int32_t* __restrict__ seq_lens, int batch,
                                                                  int H, int rows, int chunk, int S_max, int RQ,
-                                                                 int2* __restrict__ items, int* __restrict__ n_items) {
+                                                                 int* __restrict__ hdr, int2* __restrict__ items,
+                                                                 int2* __restrict__ grp) {
+  __shared__ int bins[kListBins];
   __shared__ int tot[kListThreads];
+  __shared__ int n_groups, xcount[8], xstart[8];
   const int tid = threadIdx.x;
+  for (int i = tid; i < kListBins; i += kListThreads) bins[i] = 0;
+  __syncthreads();
   const int per = (batch + kListThreads - 1) / kListThreads;
   const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
   auto groups = [&](int b) { return min(RQ, ((cu_q[b + 1] - cu_q[b]) * H + rows - 1) / rows); };
   auto splits = [&](int b) { return min(S_max, (seq_lens[b] + chunk - 1) / chunk); };
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += max(0, groups(b)) * max(0, splits(b));
-  tot[tid] = mine;
+  auto tiles = [&](int b, int sp) { return (min(chunk, seq_lens[b] - sp * chunk) + 31) / 32; };
+  // histogram of the splits' tile counts
+  for (int b = b0; b < b1; ++b) {
+    if (groups(b) <= 0) continue;
+    const int ns = splits(b);
+    for (int sp = 0; sp < ns; ++sp) atomicAdd(&bins[tiles(b, sp)], 1);
+  }
   __syncthreads();
-  for (int off = 1; off < kListThreads; off <<= 1) {
+  // first rank of each tile count, largest count first: a block-wide scan
+  // with thread t on count kListBins - 1 - t
+  const int cnt = tid < kListBins ? bins[kListBins - 1 - tid] : 0;
+  tot[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kListBins; off <<= 1) {
     const int v = tid >= off ? tot[tid - off] : 0;
     __syncthreads();
     tot[tid] += v;
     __syncthreads();
   }
-  int pos = tot[tid] - mine;
+  if (tid < kListBins) bins[kListBins - 1 - tid] = tot[tid] - cnt;
+  if (tid == kListBins - 1) n_groups = tot[tid];
+  __syncthreads();
   for (int b = b0; b < b1; ++b) {
-    const int ng = groups(b), ns = splits(b);
-    for (int sp = 0; sp < ns; ++sp)
-      for (int rq = 0; rq < ng; ++rq) items[pos++] = make_int2(b, (sp << 12) | rq);
+    const int ng = groups(b);
+    if (ng <= 0) continue;
+    const int ns = splits(b);
+    for (int sp = 0; sp < ns; ++sp) {
+      const int r = atomicAdd(&bins[tiles(b, sp)], 1);
+      grp[r] = make_int2(b, (sp << 12) | (ng - 1));
+    }
   }
-  if (tid == kListThreads - 1) n_items[0] = tot[tid];
+  __threadfence_block();
+  __syncthreads();
+  // XCD x = tid / 128 takes its splits j = 0, 1, ... (rank 16 (j / 2) + x for
+  // even j, + 15 - x for odd j); 128 threads per XCD each take a contiguous
+  // range of j, and a scan of their row-group counts places their items
+  const int G = n_groups;
+  const int x = tid >> 7, lt = tid & 127;
+  const int rem = G % 16;
+  const int gx = 2 * (G / 16) + (x < rem ? 1 : 0) + (15 - x < rem ? 1 : 0);
+  auto rank = [&](int j) { return 16 * (j >> 1) + ((j & 1) ? 15 - x : x); };
+  const int jper = (gx + 127) / 128;
+  const int j0 = min(gx, lt * jper), j1 = min(gx, j0 + jper);
+  int mine = 0;
+  for (int j = j0; j < j1; ++j) mine += (grp[rank(j)].y & 4095) + 1;
+  tot[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 128; off <<= 1) {
+    const int v = lt >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  if (lt == 127) xcount[x] = tot[tid];
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int y = 0; y < 8; ++y) {
+      xstart[y] = acc;
+      hdr[1 + y] = xcount[y];
+      hdr[9 + y] = acc;
+      acc += xcount[y];
+    }
+    hdr[0] = acc;
+  }
+  __syncthreads();
+  int pos = xstart[x] + tot[tid] - mine;
+  for (int j = j0; j < j1; ++j) {
+    const int2 g = grp[rank(j)];
+    const int sp = g.y >> 12, ng = (g.y & 4095) + 1;
+    for (int rq = 0; rq < ng; ++rq) items[pos++] = make_int2(g.x, (sp << 12) | rq);
+  }
 }
 
 }  // namespace
@@ -573,23 +640,24 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
   if (elem == 2) {
     const int nblocks = batch * plan.S_max * plan.RQ;
     const int2* items = nullptr;
-    const int* n_items = nullptr;
+    const int* list_hdr = nullptr;
     if (plan.list && (plan.NB == 8 || plan.NB == 128)) {
-      int* count = reinterpret_cast<int*>(work);
-      int2* list = reinterpret_cast<int2*>(count + 2);
+      int* hdr = reinterpret_cast<int*>(work);
+      int2* list = reinterpret_cast<int2*>(hdr + kListHeaderInts);
+      int2* grp = list + (size_t)batch * plan.S_max * plan.RQ;
       work_list_kernel<<<1, kListThreads, 0, st>>>(cu_q, seq_lens, batch, H, plan.NB == 128 ? 128 : 64,
-                                                   plan.chunk, plan.S_max, plan.RQ, list, count);
+                                                   plan.chunk, plan.S_max, plan.RQ, hdr, list, grp);
       items = list;
-      n_items = count;
+      list_hdr = hdr;
     }
     switch (plan.NB) {
       case 8:
         launch_splitkv_x8(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                          page_size, opart, lse, fp8, items, n_items, st);
+                          page_size, opart, lse, fp8, items, list_hdr, st);
         break;
       case 128:
         launch_splitkv_r128(plan, abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, Tq, H,
-                            page_size, opart, lse, items, n_items, st);
+                            page_size, opart, lse, items, list_hdr, st);
         break;
       default:
         if (fp8)

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
     bf16* __restrict__ opart, float* __restrict__ lse, const int2* __restrict__ items,
-    const int* __restrict__ n_items) {
+    const int* __restrict__ list_hdr) {
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kRBuf][kTileTok * kD];
   // swap slot of wave w: first w's partial scores of row block w ^ 1 (16
   // registers x 64 lanes, fp32), then row block w ^ 1's probabilities
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
   __shared__ __attribute__((aligned(1024))) float xs[4][16 * 64];
 
   int b, s, rq;
-  if (!split_work_item(items, n_items, batch, S_max, RQ, &b, &s, &rq)) return;
+  if (!split_work_item(items, list_hdr, batch, S_max, RQ, &b, &s, &rq)) return;
 
   const int q0 = cu_q[b];
   const int Lq = cu_q[b + 1] - q0;
@@ -575,11 +575,11 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_r128_kernel(
 void launch_splitkv_r128(const SplitPlan& plan, const void* abuf, const void* cache,
                          const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                          int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                         float* lse, const int2* items, const int* n_items, hipStream_t st) {
-  const int nblocks = batch * plan.S_max * plan.RQ;
+                         float* lse, const int2* items, const int* list_hdr, hipStream_t st) {
+  const int nblocks = items ? work_list_grid(batch, plan) : batch * plan.S_max * plan.RQ;
   splitkv_bf16_r128_kernel<<<nblocks, 256, 0, st>>>(
       (const bf16*)abuf, (const bf16*)cache, cu_q, seq_lens, page_table, max_pages, batch, H,
-      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, n_items);
+      page_size, plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, list_hdr);
 }
 
 }  // namespace mla

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, int Tq,
     bf16* __restrict__ opart, float* __restrict__ lse, const int2* __restrict__ items,
-    const int* __restrict__ n_items) {
+    const int* __restrict__ list_hdr) {
   constexpr int kBuf = F8 ? 3 : kX8Buf;
   __shared__ __attribute__((aligned(1024))) bf16 tiles[kBuf][kTileTok * kD];
   __shared__ __attribute__((aligned(1024))) char stage[F8 ? 2 : 1][F8 ? kF8StageBytes : 16];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
   __shared__ int pages_s[kMaxChunkPages];
 
   int b, s, rq;
-  if (!split_work_item(items, n_items, batch, S_max, RQ, &b, &s, &rq)) return;
+  if (!split_work_item(items, list_hdr, batch, S_max, RQ, &b, &s, &rq)) return;
 
   const int q0 = cu_q[b];
   const int Lq = cu_q[b + 1] - q0;
@@ -467,16 +467,16 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
 void launch_splitkv_x8(const SplitPlan& plan, const void* abuf, const void* cache,
                        const int32_t* cu_q, const int32_t* seq_lens, const int32_t* page_table,
                        int max_pages, int batch, int Tq, int H, int page_size, void* opart,
-                       float* lse, bool fp8, const int2* items, const int* n_items, hipStream_t st) {
-  const int nblocks = batch * plan.S_max * plan.RQ;
+                       float* lse, bool fp8, const int2* items, const int* list_hdr, hipStream_t st) {
+  const int nblocks = items ? work_list_grid(batch, plan) : batch * plan.S_max * plan.RQ;
   if (fp8)
     splitkv_bf16_x8_kernel<true><<<nblocks, 512, 0, st>>>(
         (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, n_items);
+        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, list_hdr);
   else
     splitkv_bf16_x8_kernel<false><<<nblocks, 512, 0, st>>>(
         (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, n_items);
+        plan.chunk, plan.S_max, plan.RQ, Tq, (bf16*)opart, lse, items, list_hdr);
 }
 
 }  // namespace mla

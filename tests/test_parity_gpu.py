@@ -110,6 +110,22 @@ def test_work_list_ragged(rows):
     assert torch.equal(out, again), "work-list launch not deterministic"
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+def test_work_list_balanced(rows):
+    """The work list ranks the splits by length and deals them over the
+    XCDs: splits of many lengths (512-token splits of contexts up to 2500,
+    so up to five per sequence and several rounds of sixteen), both row-group
+    sizes, heads from every row group of every sequence against the oracle,
+    and the same output on a second launch."""
+    wl = workload("dsv2_ragged_paged_256", name=f"worklist_balanced_{rows}", shape=SMALL_DSV2, batch=33,
+                  max_prefix=2500)
+    case, out = _run(wl, kv_chunk=512, rows=rows)
+    _check(case, out, heads=[0, 63, 64, 127], tag=f"balanced work list rows={rows}")
+    again = case.decode(kv_chunk=512)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "work-list launch not deterministic"
+
+
 def test_attention_rows_override_is_validated():
     import mla_compressed_latent_amd as mla
     case = GpuCase(workload("dsv2_b32_ctx4096", name="rows_arg", shape=SMALL_DSV2, batch=1, fixed_prefix=16))
