@@ -217,6 +217,20 @@ def test_many_splits_separate_combine():
         _check(case, out128, heads=heads, tag=f"many_splits chunk={chunk} rows=128")
 
 
+def test_split_limit():
+    """The planner's largest split count: a 65536-token context in 64-token
+    splits is 1024 splits of two 64-row groups (a launch from the balanced
+    work list, the separate combine with 1024 split weights staged on
+    chip), sampled heads of both row groups against the oracle; one token
+    more needs 1025 splits and the planner refuses it."""
+    import mla_compressed_latent_amd as mla
+    wl = workload("dsv2_b32_ctx4096", name="split_limit", shape=SMALL_DSV2, batch=1, fixed_prefix=65535)
+    case, out = _run(wl, kv_chunk=64)
+    _check(case, out, heads=[0, 63, 64, 127], tag="1024 splits of 64 tokens")
+    assert mla.mla_decode_workspace_bytes(case.layer, 1, 1, 1, 64 * 1024, 64) > 0
+    assert mla.mla_decode_workspace_bytes(case.layer, 1, 1, 1, 64 * 1024 + 1, 64) == 0
+
+
 def test_split_plan_of_the_benchmarked_shapes():
     """The planner's split sizes for the benchmarked decode shapes on a
     256-CU MI355X (one wave of workgroups, splits up to 8192 tokens; 128-row
