@@ -30,9 +30,11 @@
 // value waves copy each FP8 tile to staging one tile ahead (and convert tile
 // 0 before the loop); the score waves convert all of tile it+1 -- four
 // latent items and one rope item per lane, its staging reads issued before
-// their score MFMAs of tile it and the conversions spread between them -- so
-// that the conversion runs under matrix work instead of on the value waves'
-// chain (measured there: 1.5-1.7k of a 3.5k-clock tile).  Score and value waves run separate loops with the same
+// their score MFMAs of tile it, the conversions and writes after their
+// softmax, where they would otherwise wait at the barrier for the value
+// waves (on the value waves' chain the conversion measured 1.5-1.7k of a
+// 3.5k-clock tile; spread between the score MFMAs its LDS writes held up
+// the operand reads).  Score and value waves run separate loops with the same
 // barrier sequence, so their operands (query, O) can share the AGPR file.
 #include "attn_tile.hpp"
 #include "common.hpp"
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       // codes 16 (i % 32) .. + 15 -> bf16 chunks 2 (i % 32), + 1) and rope
       // item 64 wave + lane (row i / 8, chunk 64 + i % 8); rows past the
       // tile's valid rows are written as zeros.  Their staging reads go out
-      // now, the conversions and writes between the score MFMAs below.
+      // now, the conversions and writes after this tile's softmax.
       const u32x4 zero4 = {0u, 0u, 0u, 0u};
       u32x4 cw[4], rw = zero4;
       float cs[4];
@@ -200,15 +202,6 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
               a[m] = *reinterpret_cast<const bf16x8*>(tileb + a_base[m][(st + kX8Ring) & 1] +
                                                       128 * ((st + kX8Ring) >> 1));
           }
-          if constexpr (F8) {
-            if (conv) {
-              if (st == 2 || st == 6 || st == 10 || st == 14) put_latent((st - 2) / 4);
-              if (st == 16) {
-                const int i = 64 * wave + lane, t = i >> 3;
-                *reinterpret_cast<u32x4*>(ctile + (t * kChunks + 64 + ((i & 7) ^ swz(t))) * 16) = rw;
-              }
-            }
-          }
         }
         qk16_drain(acc[0], acc[1]);
       }
@@ -247,6 +240,14 @@ __global__ __launch_bounds__(512, 1) void splitkv_bf16_x8_kernel(
       l_run = l_run * alpha + rs;
       m_run = m_new;
       if (G == 0) alpha_s[it & 1][16 * wave + c16] = alpha;
+      if constexpr (F8) {   // tile it+1's conversion, in the time the barrier would otherwise take
+        if (conv) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) put_latent(u);
+          const int i = 64 * wave + lane, t = i >> 3;
+          *reinterpret_cast<u32x4*>(ctile + (t * kChunks + 64 + ((i & 7) ^ swz(t))) * 16) = rw;
+        }
+      }
     }
     if (G == 0) lrow_s[16 * wave + c16] = l_run;
     __syncthreads();   // row sums published
