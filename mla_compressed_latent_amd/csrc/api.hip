@@ -159,6 +159,9 @@ bool make_plan(const mla_layer* L, int batch, int max_q_len, int max_seq_len, in
   // many that exit at once, interleaved with the busy ones).
   p->list = (p->NB == 8 || p->NB == 128) && p->RQ <= 4096 &&
             (int64_t)batch * p->S_max * p->RQ > L->num_cus;
+  // the launch grid (at most twice the full grid with a work list) stays an int
+  const int64_t grid = (int64_t)batch * p->S_max * p->RQ;
+  if (2 * grid + (int64_t)16 * p->RQ > INT32_MAX) return false;
   return p->S_max <= 1024;   // split weights of one row are staged on chip
 }
 

@@ -222,13 +222,16 @@ def test_split_limit():
     splits is 1024 splits of two 64-row groups (a launch from the balanced
     work list, the separate combine with 1024 split weights staged on
     chip), sampled heads of both row groups against the oracle; one token
-    more needs 1025 splits and the planner refuses it."""
+    more needs 1025 splits and the planner refuses it, as it refuses a launch
+    grid past the int range."""
     import mla_compressed_latent_amd as mla
     wl = workload("dsv2_b32_ctx4096", name="split_limit", shape=SMALL_DSV2, batch=1, fixed_prefix=65535)
     case, out = _run(wl, kv_chunk=64)
     _check(case, out, heads=[0, 63, 64, 127], tag="1024 splits of 64 tokens")
     assert mla.mla_decode_workspace_bytes(case.layer, 1, 1, 1, 64 * 1024, 64) > 0
     assert mla.mla_decode_workspace_bytes(case.layer, 1, 1, 1, 64 * 1024 + 1, 64) == 0
+    # a launch grid past 2^31 workgroups is refused too (2^21 sequences x 1024 splits x 2 row groups)
+    assert mla.mla_decode_workspace_bytes(case.layer, 1 << 21, 1 << 21, 1, 64 * 1024, 64) == 0
 
 
 def test_split_plan_of_the_benchmarked_shapes():
