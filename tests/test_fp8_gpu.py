@@ -137,6 +137,18 @@ def test_fp8_decode_parity(shape, kv_chunk):
     _check(case, out, f"decode heads={shape.H} chunk={kv_chunk}")
 
 
+def test_fp8_work_list():
+    """FP8 pages on a ragged decode batch larger than one wave of workgroups
+    (40 sequences, 64-token splits): the eight-wave kernel launched from the
+    balanced work list, heads of every row group against the oracle."""
+    wl = workload("dsv2_ragged_paged_256", name="fp8_work_list", shape=FP8_DSV2, batch=40,
+                  max_prefix=600, prefix_source="hidden", seed=35)
+    case = _case(wl)
+    out = case.decode(kv_chunk=64)
+    torch.cuda.synchronize()
+    _check(case, out, "decode work list chunk=64", heads=[0, 63, 64, 127])
+
+
 def test_fp8_deterministic():
     wl = workload("dsv2_ragged_paged_256", name="fp8_det", shape=FP8_DSV2, batch=3, max_prefix=400,
                   prefix_source="hidden", seed=33)
