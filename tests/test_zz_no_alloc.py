@@ -1,7 +1,7 @@
 """mla_decode_no_alloc (the decode entry point that works in the library's
 static device scratch) against mla_decode on the same inputs: two calls in a
 row, the second with a smaller batch, for the bf16 kernels of both row
-blockings and for an fp32 layer, and the rejection of a call whose workspace
+blockings, for FP8 pages and for an fp32 layer, and the rejection of a call whose workspace
 exceeds the scratch.  Both entry points run the same kernels with the same
 split plan, so their outputs must be bit-identical."""
 import dataclasses
@@ -73,6 +73,19 @@ def test_no_alloc_with_work_list():
     # them, so the list is used) in 31 MB of scratch
     ref, got = _both(case, kv_chunk=128)
     assert torch.equal(ref, got)
+
+
+def test_no_alloc_fp8_pages_two_calls():
+    """FP8 pages (the eight-wave kernel's converting path), two calls in a
+    row, the second with a smaller batch."""
+    fp8 = dataclasses.replace(SMALL_DSV2, cache_format="fp8")
+    for batch, prefix in ((5, 900), (2, 200)):
+        wl = workload("dsv2_ragged_paged_256", name=f"noalloc_fp8_b{batch}", shape=fp8, batch=batch,
+                      max_prefix=prefix, prefix_source="hidden", seed=40 + batch)
+        print(f"[no_alloc] {wl.name} B={wl.batch}", flush=True)
+        case = _case(wl, 0)
+        ref, got = _both(case, kv_chunk=64)
+        assert torch.equal(ref, got), f"{wl.name}: no-alloc output differs from mla_decode"
 
 
 def test_no_alloc_fp32_layer_two_calls():
