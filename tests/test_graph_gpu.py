@@ -14,22 +14,25 @@ if not torch.cuda.is_available():  # pragma: no cover
 from gpu_harness import GpuCase  # noqa: E402
 
 
-def test_graph_replay_matches_eager():
-    wl = workload("dsv2_ragged_paged_256", name="graph", batch=5, max_prefix=300)
+@pytest.mark.parametrize("batch,max_prefix,kv_chunk", [(5, 300, 128), (40, 400, 64)], ids=["grid", "work_list"])
+def test_graph_replay_matches_eager(batch, max_prefix, kv_chunk):
+    """kv_chunk 64 over 40 ragged sequences launches the attention from the
+    device-built work list, which every replay rebuilds."""
+    wl = workload("dsv2_ragged_paged_256", name=f"graph_b{batch}", batch=batch, max_prefix=max_prefix)
     print(f"[graph] case {wl.name} B={wl.batch}", flush=True)
     case = GpuCase(wl)
     mla = case.mla
     s = wl.shape
     Tq = case.q.shape[0]
     ws = torch.empty(mla.mla_decode_workspace_bytes(case.layer, wl.batch, Tq, case.max_q_len,
-                                                    case.max_seq_len, 128), dtype=torch.uint8, device="cuda")
+                                                    case.max_seq_len, kv_chunk), dtype=torch.uint8, device="cuda")
     aws = torch.empty(max(1, mla.mla_append_workspace_bytes(case.layer, Tq)), dtype=torch.uint8, device="cuda")
 
     def step(out, stream=None):
         mla.mla_append_latent(case.layer, case.x_new_dev, case.cu_q, case.prefix_dev, case.page_table, case.cache,
                               workspace=aws, stream=stream)
         mla.mla_decode(case.layer, case.q_dev, case.cu_q, case.seq_lens, case.page_table, case.cache, out,
-                       case.max_q_len, case.max_seq_len, kv_chunk=128, workspace=ws, stream=stream)
+                       case.max_q_len, case.max_seq_len, kv_chunk=kv_chunk, workspace=ws, stream=stream)
 
     eager = torch.empty((Tq, s.H, s.d_v), dtype=case.dt, device="cuda")
     step(eager)
