@@ -7,7 +7,8 @@ device arithmetic runs in a different grouping of launches).  One case is
 also checked against the float64 oracle to the decode parity tolerances.
 Covered: both split-KV kernels (16 and 128 heads), one and two queries per
 sequence, paged and contiguous caches, FP8 pages, every absorb weight
-blocking (d_nope 64, 128, 192), and an fp32 layer (no fused launch)."""
+blocking (d_nope 64, 128, 192), an fp32 layer (no fused launch), and a
+step with no new tokens (the decode alone, the cache untouched)."""
 import dataclasses
 
 import numpy as np
@@ -113,3 +114,22 @@ def test_step_workspace_checked():
     assert ei.value.status == mla.MLA_ERR_INSUFFICIENT_WORKSPACE
     torch.cuda.synchronize()
     assert torch.equal(_bits(case.cache), _bits(before)), "a rejected call wrote the cache"
+
+
+def test_step_without_new_tokens():
+    """total_new = 0: no append work, the cache is left as it is and the
+    output equals mla_decode's bit for bit."""
+    wl = workload("dsv2_b32_ctx4096", name="step_no_new", shape=SMALL_DSV2, batch=3, fixed_prefix=None,
+                  max_prefix=500, paging="random", spare_page_frac=0.2)
+    case = GpuCase(wl)
+    case.append_new()
+    ref = case.decode()
+    torch.cuda.synchronize()
+    before = case.cache.clone()
+    out = torch.full_like(ref, float("nan"))
+    no_new = torch.zeros(wl.batch + 1, dtype=torch.int32, device="cuda")
+    mla.mla_decode_step(case.layer, case.x_new_dev[:0], no_new, case.seq_lens, case.q_dev, case.cu_q,
+                        case.seq_lens, case.page_table, case.cache, out, case.max_q_len, case.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(ref)), "decode step without new tokens differs from mla_decode"
+    assert torch.equal(_bits(case.cache), _bits(before)), "decode step without new tokens changed the cache"
