@@ -37,11 +37,11 @@ EXTEND_METRIC = "MLA chunked-extend / prefill query tokens/s and matrix-core TFL
 # the kernel source they were taken on and the workload (profiles/ holds the
 # runs).  A changed kernel reports null until counters are taken again.
 MEASURED_TRAFFIC = {
-    ("3e0ae54f2865317d", "dsv2_b32_ctx4096"): {"fetch_bytes": 155951825, "write_bytes": 16842757},
-    ("3e0ae54f2865317d", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606639291, "write_bytes": 16860025},
-    ("3e0ae54f2865317d", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210609184, "write_bytes": 35258368},
-    ("3e0ae54f2865317d", "dsv2_ragged_paged_256"): {"fetch_bytes": 5131979406, "write_bytes": 124762154},
-    ("3e0ae54f2865317d", "dsv2_b32_ctx4096_fp8"): {"fetch_bytes": 89418183, "write_bytes": 16842762},
+    ("8d4c951127b547e1", "dsv2_b32_ctx4096"): {"fetch_bytes": 155951825, "write_bytes": 16842763},
+    ("8d4c951127b547e1", "llama2_7b_mla_b64_ctx8192"): {"fetch_bytes": 606661307, "write_bytes": 8421376},
+    ("8d4c951127b547e1", "dsv2_b8_ctx131072"): {"fetch_bytes": 1210617024, "write_bytes": 35258368},
+    ("8d4c951127b547e1", "dsv2_ragged_paged_256"): {"fetch_bytes": 5128679836, "write_bytes": 124757703},
+    ("8d4c951127b547e1", "dsv2_b32_ctx4096_fp8"): {"fetch_bytes": 89418305, "write_bytes": 16842865},
 }
 
 

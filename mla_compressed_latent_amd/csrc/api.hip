@@ -176,7 +176,7 @@ DecodeLayout decode_layout(const mla_layer* L, int batch, int total_q, const mla
   DecodeLayout d;
   d.off_abuf = 0;
   d.off_opart = align256(rows * D * L->elem);
-  const size_t part_elem = p.NB >= 8 ? 2 : 4;   // the 64- and 128-row kernels write bf16 partials
+  const size_t part_elem = L->elem == 2 ? 2 : 4;   // bf16 layers' split-KV kernels write bf16 partials
   d.off_lse = d.off_opart + align256((size_t)p.S_max * rows * c.kv_lora_rank * part_elem);
   d.off_olat = d.off_lse + align256((size_t)p.S_max * rows * 4);
   d.off_work = d.off_olat + align256(rows * c.kv_lora_rank * L->elem);
@@ -280,9 +280,9 @@ void decode_launch(const mla_layer* L, const void* q, const int32_t* cu_q, const
                         c.kv_lora_rank, c.qk_rope_head_dim, c.page_size, L->scale, opart, lse,
                         c.cache_format == MLA_CACHE_FP8, ws + d.off_work, st);
   if (phases & MLA_PHASE_OUTPUT) {
-    const bool part_bf16 = p.NB >= 8;   // the 64- and 128-row kernels write bf16 partials
+    const bool part_bf16 = L->elem == 2;   // bf16 layers' split-KV kernels write bf16 partials
     if (L->elem == 2 && p.S_max <= mla::kCombineMaxSplits) {
-      mla::launch_combine_out(p, opart, part_bf16, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
+      mla::launch_combine_out(p, opart, lse, cu_q, seq_lens, L->wuv_p, out, batch, total_q, H,
                               c.v_head_dim, L->num_cus, st);
     } else {
       mla::launch_combine(L->elem, p, opart, part_bf16, lse, cu_q, seq_lens, batch, total_q, H,
@@ -873,7 +873,7 @@ mla_status mla_decode_project(const mla_layer* L, const void* q, const int32_t* 
     mla::SplitPlan p;
     make_plan(L, batch, max_q_len, max_seq_len, 0, &p);
     const DecodeLayout d = decode_layout(L, batch, total_q, p);
-    mla::launch_combine(L->elem, p, ws + d.off_opart, p.NB >= 8, (const float*)(ws + d.off_lse), cu_q,
+    mla::launch_combine(L->elem, p, ws + d.off_opart, L->elem == 2, (const float*)(ws + d.off_lse), cu_q,
                         seq_lens, batch, total_q, c.num_attention_heads, c.kv_lora_rank, ws + d.off_olat, st);
     act = ws + d.off_olat;
   }

@@ -262,14 +262,9 @@ __global__ __launch_bounds__(64) void out_proj_bf16_kernel(const bf16* __restric
 constexpr int kCombThreads = 512;
 constexpr int kCombRowPad = 8;   // bf16 pad per LDS row of o_lat
 
-// E consecutive elements of a split partial row, loaded as one vector (16
-// bytes, or 8 for bf16 partials in blocks of 4 tokens) and read as floats.
+// E consecutive elements of a bf16 split partial row, loaded as one vector
+// (16 bytes, or 8 in blocks of 4 tokens) and read as floats.
 template <typename P, int E> struct PartVec;
-template <> struct PartVec<float, 4> {
-  typedef f32x4 T;
-  static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const T*>(p); }
-  static __device__ __forceinline__ float get(const T& v, int e) { return v[e]; }
-};
 template <> struct PartVec<bf16, 4> {
   typedef __bf16 T __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ T load(const bf16* p) { return *reinterpret_cast<const T*>(p); }
@@ -628,7 +623,7 @@ void launch_out_proj(int elem, const void* olat, const void* wuv, void* out, int
   }
 }
 
-void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
+void launch_combine_out(const SplitPlan& plan, const void* opart, const float* lse,
                         const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
                         int batch, int Tq, int H, int dv, int num_cus, hipStream_t st) {
   // the largest token block that still gives every compute unit a workgroup
@@ -636,16 +631,11 @@ void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16
   while (TB > 4 && (int64_t)((Tq + TB - 1) / TB) * H < num_cus) TB /= 2;
   const unsigned blocks = (unsigned)(((Tq + TB - 1) / TB) * H);
   switch (TB) {
-#define MLA_COMBINE_CASE(N)                                                                     \
-  case N:                                                                                       \
-    if (part_bf16)                                                                              \
-      combine_out_bf16_kernel<N, bf16><<<blocks, kCombThreads, 0, st>>>(                        \
-          (const bf16*)opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H,  \
-          dv, plan.chunk, plan.S_max);                                                          \
-    else                                                                                        \
-      combine_out_bf16_kernel<N, float><<<blocks, kCombThreads, 0, st>>>(                       \
-          (const float*)opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H, \
-          dv, plan.chunk, plan.S_max);                                                          \
+#define MLA_COMBINE_CASE(N)                                                                    \
+  case N:                                                                                      \
+    combine_out_bf16_kernel<N, bf16><<<blocks, kCombThreads, 0, st>>>(                         \
+        (const bf16*)opart, lse, cu_q, seq_lens, (const bf16*)wuv, (bf16*)out, batch, Tq, H, dv, \
+        plan.chunk, plan.S_max);                                                               \
     break;
     MLA_COMBINE_CASE(32) MLA_COMBINE_CASE(16) MLA_COMBINE_CASE(8) MLA_COMBINE_CASE(4)
 #undef MLA_COMBINE_CASE

@@ -108,8 +108,8 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
 // out[t][h][:] = (LSE-weighted merge of the split partials) . W_uv_h, one
 // workgroup per (32 query tokens, head); bf16 layers, at most kCombineMaxSplits.
 constexpr int kCombineMaxSplits = 64;
-// part_bf16: the partials are bf16 (the 64- and 128-row kernels'), else fp32.
-void launch_combine_out(const SplitPlan& plan, const void* opart, bool part_bf16, const float* lse,
+// The partials are bf16 (every bf16 layer's split-KV kernel writes them so).
+void launch_combine_out(const SplitPlan& plan, const void* opart, const float* lse,
                         const int32_t* cu_q, const int32_t* seq_lens, const void* wuv, void* out,
                         int batch, int Tq, int H, int dv, int num_cus, hipStream_t st);
 // 64 query rows per workgroup, eight waves (bf16 layers, plan.NB == 8);

@@ -9,7 +9,8 @@
 // which is "still softmax(Q K^T / sqrt d) V with K factored" (section
 // "Absorption: the part that makes it free").  Each workgroup takes one
 // chunk of one sequence's tokens ("split"), keeps a running max and sum per
-// row (online softmax), and leaves a normalised partial O and its log-sum-exp;
+// row (online softmax), and leaves a normalised partial O (bf16 for bf16
+// layers, rounded once from the fp32 accumulators) and its log-sum-exp;
 // the combine kernel merges the splits.
 //
 // bf16 path, at most 32 rows per sequence (d_c = 512, d_rope = 64; more rows
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const bf16* __restrict__ abuf, const void* __restrict__ cache_v, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int max_pages,
     int batch, int H, int page_size, int chunk, int S_max, int RQ, float scale_log2e, int Tq,
-    float* __restrict__ opart, float* __restrict__ lse) {
+    bf16* __restrict__ opart, float* __restrict__ lse) {
   static_assert(NB == 1, "one 32-row block per workgroup");
   constexpr int kDbPerPv = kDC / 32 / 2;       // 32-wide value blocks per value wave (8)
   constexpr int kBuf = F8 ? 3 : kNBuf;
@@ -380,15 +381,30 @@ __global__ __launch_bounds__(256, 1) void splitkv_bf16_kernel(
     const float lr = lrow_s[rb][l32];
     const float inv = lr > 0.f ? 1.f / lr : 0.f;
     const int64_t rowg = (int64_t)(q0 + row / H) * H + row % H;
-    float* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + pw * 256;
+    bf16* dst = opart + ((int64_t)s * rows_total + rowg) * kDC + pw * 256;
+    // lane half g holds columns 8 q4 + 4 g .. + 3; one swap of the lane
+    // halves per dword gives the lower half all of group q4 = 2p and the
+    // upper half all of group 2p + 1, written as 16 bytes per lane
 #pragma unroll
     for (int db = 0; db < kDbPerPv; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v;
+      for (int p = 0; p < 2; ++p) {
+        uint32_t a[2], bq[2];   // groups 2p (a) and 2p + 1 (bq), this lane's 4 columns as 2 dwords
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = O[db][rb][4 * q4 + e] * inv;
-        *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * q4 + 4 * g) = v;
+        for (int k = 0; k < 2; ++k) {
+          a[k] = pack_bf16x2(O[db][rb][8 * p + 2 * k] * inv, O[db][rb][8 * p + 2 * k + 1] * inv);
+          bq[k] = pack_bf16x2(O[db][rb][8 * p + 4 + 2 * k] * inv, O[db][rb][8 * p + 4 + 2 * k + 1] * inv);
+        }
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t send = g ? a[k] : bq[k];
+          const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+          const uint32_t got = g ? r[0] : r[1];   // the other half's dword
+          w[k] = g ? got : a[k];
+          w[2 + k] = g ? bq[k] : got;
+        }
+        *reinterpret_cast<u32x4*>(dst + 32 * db + 16 * p + 8 * g) = w;
       }
   }
 }
@@ -663,11 +679,11 @@ void launch_splitkv(int elem, const SplitPlan& plan, const void* abuf, const voi
         if (fp8)
           splitkv_bf16_kernel<1, true><<<nblocks, 256, 0, st>>>(
               (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
+              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, (bf16*)opart, lse);
         else
           splitkv_bf16_kernel<1, false><<<nblocks, 256, 0, st>>>(
               (const bf16*)abuf, cache, cu_q, seq_lens, page_table, max_pages, batch, H, page_size,
-              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, opart, lse);
+              plan.chunk, plan.S_max, plan.RQ, scale_log2e, Tq, (bf16*)opart, lse);
         break;
     }
   } else {

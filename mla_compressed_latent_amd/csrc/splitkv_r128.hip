@@ -8,9 +8,9 @@
 //     S[row][t]  = scale * A[row] . cache[t]          (K = 576)
 //     O[row][:] += softmax_t(S) cache[t][:512]        (K = tokens)
 // with an online softmax per row and normalised partials + log2-sum-exp per
-// (row, split).  Partials are bf16 ([split][row][512], as the 64-row
-// kernel's; the 32-row and fp32 kernels write fp32), rounded once from the
-// fp32 accumulators.
+// (row, split).  Partials are bf16 ([split][row][512], as those of the
+// 64- and 32-row kernels; the fp32 kernel writes fp32), rounded once from
+// the fp32 accumulators.
 //
 // All matrix work is on the 32x32x16 bf16 instruction.  Wave w (pair
 // p = w / 2, half d = w % 2):
