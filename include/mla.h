@@ -221,7 +221,10 @@ size_t mla_decode_workspace_bytes(const mla_layer* layer, int32_t batch, int32_t
  *   out       [total_q][H][d_v] device: out = softmax(score) V per head,
  *             computed as (sum_t w_t c_t) W_uv_h; no output projection.
  *   kv_chunk  tokens per split-KV work item, a multiple of 64 up to 8192, or
- *             0 (auto); at most 1024 splits per sequence.
+ *             0 (auto); at most 1024 splits per sequence, and batch x splits
+ *             x row groups (64 or 128 rows each) below 2^30 workgroups: a
+ *             call past either limit fails with INVALID_ARG (and
+ *             mla_decode_workspace_bytes returns 0).
  *             The split plan depends only on host arguments, so results are
  *             run-to-run deterministic.
  *   workspace device, >= mla_decode_workspace_bytes(...) bytes
