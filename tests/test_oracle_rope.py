@@ -75,3 +75,26 @@ def test_rotation_does_not_commute_with_absorption():
     wrong = np.array([rope_rotate(w_uk @ q, p, 10000.0) @ c[t] for t in range(n)])
     assert np.max(np.abs(correct - wrong)) > 1.0
     assert not np.array_equal(np.argsort(correct), np.argsort(wrong))
+
+
+def test_latent_rows_rotate_only_the_rope_block_at_each_tokens_position():
+    """The cached row [c | k_rope] of a token: c = x W_dkv unrotated, k_rope =
+    the tail of x W_dkv turned pair by pair by position * base**(-2i/d_rope),
+    written here as multiplication by a complex exponential."""
+    from oracle.mla_oracle import latent_rows
+
+    rng = np.random.default_rng(17)
+    d_model, d_c, d_rope, base = 24, 12, 8, 10000.0
+    x = rng.standard_normal((5, d_model))
+    w = rng.standard_normal((d_model, d_c + d_rope))
+    positions = np.array([0, 1, 9, 300, 4095])
+    rows = latent_rows(x, w, positions, d_c, base)
+    u = x @ w
+    assert np.array_equal(rows[:, :d_c], u[:, :d_c])          # content block untouched
+    assert np.array_equal(rows[0], u[0])                      # position 0: no rotation
+    for t, p in enumerate(positions):
+        z = u[t, d_c::2] + 1j * u[t, d_c + 1::2]
+        turn = np.exp(1j * p * base ** (-2.0 * np.arange(d_rope // 2) / d_rope))
+        want = z * turn
+        assert rows[t, d_c::2] == pytest.approx(want.real, abs=1e-12)
+        assert rows[t, d_c + 1::2] == pytest.approx(want.imag, abs=1e-12)
