@@ -126,6 +126,19 @@ def test_work_list_balanced(rows):
     assert torch.equal(out, again), "work-list launch not deterministic"
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+def test_partial_row_groups(rows):
+    """40 heads: a one-query sequence has 40 rows and a two-query one 80, so
+    the last row group of every sequence is partly empty (24 or 48 of 64 rows
+    idle in the 64-row kernel, 88 or 48 of 128 in the 128-row one); every
+    head against the oracle."""
+    from mla_synth import Shape
+    wl = workload("dsv2_ragged_paged_256", name=f"heads40_{rows}", shape=Shape(512, 40, 128, 64, 128, 512),
+                  batch=5, max_prefix=900)
+    case, out = _run(wl, kv_chunk=256, rows=rows)
+    _check(case, out, tag=f"40 heads rows={rows}")
+
+
 def test_attention_rows_override_is_validated():
     import mla_compressed_latent_amd as mla
     case = GpuCase(workload("dsv2_b32_ctx4096", name="rows_arg", shape=SMALL_DSV2, batch=1, fixed_prefix=16))
