@@ -1,6 +1,6 @@
 """GPU: page sizes other than 64 (128 and 256 tokens) under random page
-tables, for every attention path: decode with both split-KV kernels (128 and
-32 heads), bf16 and FP8 caches, and both extend forms -- against the oracle,
+tables, for every attention path: decode with the split-KV kernels (64- and
+128-row at 128 heads, 32-row at 32 heads), bf16 and FP8 caches, and both extend forms -- against the oracle,
 bf16 tolerances as in the decode parity tests."""
 import dataclasses
 
@@ -43,6 +43,11 @@ def test_decode_page_sizes(page_size, base, fmt):
     out = case.decode(kv_chunk=128)
     torch.cuda.synchronize()
     _check(case, out, f"decode page {page_size} heads {shape.H} {fmt}")
+    if shape.H == 128 and fmt == "dtype":   # the 128-row kernel on the same pages
+        mla.mla_layer_set_attention_rows(case.layer, 128)
+        out = case.decode(kv_chunk=128)
+        torch.cuda.synchronize()
+        _check(case, out, f"decode page {page_size} heads {shape.H} {fmt} rows=128")
 
 
 @pytest.mark.parametrize("page_size", [128, 256])
