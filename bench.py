@@ -51,10 +51,10 @@ ATTENTION_SOURCES = ("attn_tile.hpp", "splitkv.hip", "splitkv_x8.hip", "splitkv_
 EXTEND_SOURCES = ("attn_tile.hpp", "extend.hip")
 # HBM bytes of one mla_extend call (both expanded kernels), measured as above.
 EXTEND_TRAFFIC = {
-    ("0008695d329dc1fc", "dsv2_extend_b4_p3072_c1024"): {
-        "fetch_bytes": 2558964580, "write_bytes": 1207988858,
-        "per_kernel": {"expand_kv": {"fetch_bytes": 1247159164, "write_bytes": 1073741824},
-                       "extend_attn": {"fetch_bytes": 1311805416, "write_bytes": 134247034}}},
+    ("ebb2cf6b8e183b98", "dsv2_extend_b4_p3072_c1024"): {
+        "fetch_bytes": 2560137011, "write_bytes": 1207989350,
+        "per_kernel": {"expand_kv": {"fetch_bytes": 1248185549, "write_bytes": 1073741824},
+                       "extend_attn": {"fetch_bytes": 1311951462, "write_bytes": 134247526}}},
 }
 
 
